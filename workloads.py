@@ -1,0 +1,77 @@
+"""Seeded synthetic inputs and the workload shapes for S2-Attn.
+
+This module is shared by the fp64 oracle's tests, the GPU parity tests and the
+benchmark.  It holds no arithmetic of the attention method itself: it only
+draws random numbers, rounds them to bfloat16 and widens bfloat16 back to
+float64, so both sides of every parity check see bit-identical inputs.
+
+Input recipe: ``numpy.random.default_rng(seed)`` (PCG64), draws in the order
+q, k, v, dout, each ``standard_normal(shape, float32)``, rounded to bfloat16
+with round-to-nearest-even.  q/dout are [B, N, H, D] and k/v are
+[B, N, Hkv, D], contiguous.  These stand in for projected LLaMA2 attention
+activations on long documents; no dataset or trained weight is used.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# Workload shapes.  Sizes are the LLaMA2-7B and 70B attention shapes the pages
+# fine-tune at (LongLoRA abstract: 7B to 100k, 70B to 32k), always with the
+# group size G = N/4 that the AIMech page's group-size limitation recommends
+# and the shift G/2 of the AIMech definition.
+WORKLOADS = {
+    "tiny_n256": dict(B=1, N=256, H=4, Hkv=4, D=64, G=64, shift=32, rope=None),
+    "llama2_7b_n8k": dict(B=1, N=8192, H=32, Hkv=32, D=128, G=2048, shift=1024, rope=None),
+    "llama2_7b_n32k": dict(B=1, N=32768, H=32, Hkv=32, D=128, G=8192, shift=4096, rope=None),
+    "llama2_7b_n100k": dict(B=1, N=102400, H=32, Hkv=32, D=128, G=25600, shift=12800, rope=None),
+    "llama2_70b_gqa_n32k_rope": dict(B=1, N=32768, H=64, Hkv=8, D=128, G=8192, shift=4096,
+                                     rope=(10000.0, 8.0)),
+}
+
+# The workload the benchmark times: LLaMA2-7B attention at 32k context.
+BENCH_WORKLOAD = "llama2_7b_n32k"
+
+
+def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (round to nearest, ties to even).
+
+    Returns the bfloat16 bit patterns as uint16.  Inputs here are finite
+    normal draws, so no NaN handling is needed; a non-finite input raises.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("bf16_bits_from_f32: non-finite input")
+    u = x.view(np.uint32).astype(np.uint64)
+    rounding_bias = 0x7FFF + ((u >> 16) & 1)
+    return ((u + rounding_bias) >> 16).astype(np.uint16)
+
+
+def f64_from_bf16_bits(bits: np.ndarray) -> np.ndarray:
+    """Widen bfloat16 bit patterns (uint16) exactly to float64."""
+    u = np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return u.view(np.float32).astype(np.float64)
+
+
+def make_inputs(B, N, H, Hkv, D, seed=0, with_dout=True, qk_prescale=None):
+    """Seeded bfloat16 inputs as uint16 bit arrays.
+
+    ``qk_prescale`` (optional float) multiplies the float32 q and k draws
+    before rounding; it changes only the data, never the method.
+    """
+    rng = np.random.default_rng(seed)
+    out = {}
+    for name, heads in (("q", H), ("k", Hkv), ("v", Hkv)):
+        x = rng.standard_normal((B, N, heads, D), dtype=np.float32)
+        if qk_prescale is not None and name in ("q", "k"):
+            x = x * np.float32(qk_prescale)
+        out[name] = bf16_bits_from_f32(x)
+    if with_dout:
+        out["dout"] = bf16_bits_from_f32(rng.standard_normal((B, N, H, D), dtype=np.float32))
+    return out
+
+
+def make_inputs_f32(B, N, H, Hkv, D, seed=0):
+    """The same draws as ``make_inputs`` before rounding (float32 arrays)."""
+    rng = np.random.default_rng(seed)
+    return {name: rng.standard_normal((B, N, heads, D), dtype=np.float32)
+            for name, heads in (("q", H), ("k", Hkv), ("v", Hkv))}
