@@ -1,0 +1,234 @@
+#!/usr/bin/env python3
+"""S2-Attn forward + backward throughput on one MI355X.
+
+One step is the whole hot path over one batch of synthetic input: the forward
+kernel, then the backward's three kernels (Delta preprocess, dK/dV, dQ), on
+the LLaMA2-7B attention shape at 32k context (B 1, N 32768, H 32, D 128,
+G 8192, shift 4096) unless --workload says otherwise.  Inputs are seeded
+N(0, 1) draws rounded to bf16 and stay resident in HBM.
+
+Throughput counts effective causal FLOPs: 2*B*H*N*G*D forward plus 2.5x that
+backward, over the wall time of K steps bracketed by device synchronisation.
+Each kernel is also bracketed by HIP events recorded on the stream the
+kernels are launched on; their average durations give the roofline of the
+dominant kernel.
+
+Prints ONE JSON line.  Options:
+  --gpus N        only 1 is supported (the path is single-GPU)
+  --steps K       timed steps (default 20)
+  --warmup W      untimed steps first (default 5)
+  --workload W    a key of workloads.WORKLOADS without RoPE
+  --no-cpu-baseline   skip timing the fp64 oracle on a sample
+  --calib-copy-mib M  also run one plain device copy of M MiB (for counter calibration)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_HBM_GBS = 8000.0
+METRIC = "S2-Attn fwd+bwd TFLOP/s and % bf16 MFMA peak, LLaMA2-7B shape N=32k G=8k"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+KERNEL_SOURCES = ["fwd.hip", "bwd.hip", "bwd_delta.hip", "staging.hpp", "device_common.hpp", "kernels.hpp"]
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "grouped_shifted_attention_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def cpu_baseline(cfg, x_bits, budget_s=20.0):
+    """Time the fp64 oracle (as it stands) on a bounded sample of the same
+    workload: whole (batch, head, group) units, forward + backward, until the
+    budget is used; report effective TFLOP/s under the same FLOP convention."""
+    import numpy as np
+
+    import oracle
+    import workloads
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [(i.get("internal_api"), i.get("num_threads")) for i in threadpool_info()]
+    except Exception:  # threadpoolctl absent
+        blas = []
+    B, N, H, Hkv, D, G, sh = (cfg[k] for k in ("B", "N", "H", "Hkv", "D", "G", "shift"))
+    units = [(h, g) for g in (0, N // G - 1) for h in (0, H // 2, H - 1, H // 2 - 1)]
+    done = 0
+    t0 = time.perf_counter()
+    for h, g in units:
+        kvh = oracle.kv_head(h, H, Hkv)
+        f64 = lambda name, hh: workloads.f64_from_bf16_bits(x_bits[name][0, :, hh, :])
+        qh, kh, vh, doh = f64("q", h), f64("k", kvh), f64("v", kvh), f64("dout", h)
+        shh = oracle.head_shift(h, H, sh)
+        oracle.head_unit_forward(qh, kh, vh, G, shh, g)
+        oracle.head_unit_backward(qh, kh, vh, doh, G, shh, g)
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = done * 7 * G * G * D  # per unit: 2 G^2 D forward + 5 G^2 D backward
+    threads = max([n for _, n in blas if n] or [1])
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{done} of {B * H * (N // G)} (batch, head, group) units of {cfg['name']}, forward + "
+                  f"backward in float64 NumPy, {dt:.1f} s; every unit does identical work, so the rate "
+                  f"is the whole workload's",
+        "host_cpus": len(os.sched_getaffinity(0)),
+        "blas": blas,
+        "seconds": dt,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0)
+    ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this S2-Attn build runs on one GPU only; no multi-GPU path exists "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world})", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workloads
+    from grouped_shifted_attention_amd import flops, ops
+
+    name = args.workload or workloads.BENCH_WORKLOAD
+    cfg = dict(workloads.WORKLOADS[name], name=name)
+    if cfg["rope"] is not None:
+        raise SystemExit("bench.py times the workloads without RoPE")
+    B, N, H, Hkv, D, G, sh = (cfg[k] for k in ("B", "N", "H", "Hkv", "D", "G", "shift"))
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    x = workloads.make_inputs(B, N, H, Hkv, D, seed=0)
+    to_gpu = lambda bits: torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    q, k, v, do = (to_gpu(x[n]) for n in ("q", "k", "v", "dout"))
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = ops.bwd_workspace(q, k)
+    stream = torch.cuda.current_stream(dev)
+
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    kernels = ["fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq"]
+
+    def step(events=None):
+        if events is not None:
+            events[0].record(stream)
+        ops.s2attn_fwd(q, k, v, G, sh, out=out, lse=lse)
+        if events is not None:
+            events[1].record(stream)
+        ops.s2attn_bwd_preprocess(out, do, ws)
+        if events is not None:
+            events[2].record(stream)
+        ops.s2attn_bwd_dkdv(q, k, v, lse, do, G, sh, ws, dk=dk, dv=dv)
+        if events is not None:
+            events[3].record(stream)
+        ops.s2attn_bwd_dq(q, k, v, lse, do, G, sh, ws, dq=dq)
+        if events is not None:
+            events[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    ms_step = (t1 - t0) * 1e3 / max(args.steps, 1)
+    kernel_ms = {kname: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) if evs else 0.0
+                 for j, kname in enumerate(kernels)}
+    f_fwd = flops.s2attn_fwd_flops(B, H, N, G, D)
+    f_bwd = flops.s2attn_bwd_flops(B, H, N, G, D)
+    value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
+
+    # MFMA work each kernel performs, in effective causal FLOPs per launch:
+    # forward 2 products, dK/dV 4 (S, dP, dV, dK), dQ 3 (S, dP, dQ).
+    unit = B * H * N * G * D
+    kernel_flops = {"fwd": 2 * unit, "bwd_dkdv": 4 * unit, "bwd_dq": 3 * unit}
+    dominant = max(kernel_flops, key=lambda kname: kernel_ms[kname])
+    achieved = kernel_flops[dominant] / (kernel_ms[dominant] * 1e-3) / 1e12
+    roofline = {
+        "bound": "mfma", "kernel": dominant, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+        "avg_launch_ms": kernel_ms[dominant],
+    }
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+        if (rec.get("kernel") == dominant and rec.get("workload") == name
+                and rec.get("source_sha256") == kernel_source_digest()):
+            roofline["traffic"] = rec["traffic_bytes"]
+    except (OSError, ValueError, KeyError):
+        pass
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": name, "B": B, "N": N, "H": H, "Hkv": Hkv, "D": D, "G": G, "shift": sh,
+                   "parallelism": "single-gpu"},
+        "pct_peak": 100.0 * value / PEAK_BF16_TFLOPS,
+        "fwd_tflops": f_fwd / (kernel_ms["fwd"] * 1e-3) / 1e12,
+        "bwd_tflops": f_bwd / (sum(kernel_ms[kk] for kk in kernels[1:]) * 1e-3) / 1e12,
+        "kernel_ms": kernel_ms,
+        "roofline": roofline,
+        "hbm_gbs_algorithmic": {
+            "fwd": flops.fwd_algorithmic_bytes(B, N, H, Hkv, D) / (kernel_ms["fwd"] * 1e-3) / 1e9,
+            "bwd": flops.bwd_algorithmic_bytes(B, N, H, Hkv, D)
+            / (sum(kernel_ms[kk] for kk in kernels[1:]) * 1e-3) / 1e9,
+            "peak": PEAK_HBM_GBS,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, x, args.cpu_budget_s)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,70 @@
+"""ctypes loader for libs2attn.so, the C-ABI library.
+
+Loading fails loudly when the library has not been built: there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+from .build import LIB_PATH
+
+S2ATTN_OK = 0
+S2ATTN_EINVAL = -1
+S2ATTN_EUNSUPPORTED = -2
+S2ATTN_EHIP = -3
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_D = ctypes.c_double
+_S = ctypes.c_size_t
+
+# name -> (restype, argtypes); mirrors include/s2attn.h
+SIGNATURES = {
+    "s2attn_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
+    "s2attn_bwd_workspace_size": (_S, [_I, _I, _I, _I, _I]),
+    "s2attn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _S, _P]),
+    "s2attn_bwd_preprocess": (_I, [_P, _P, _I, _I, _I, _I, _P, _S, _P]),
+    "s2attn_bwd_dkdv": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _S, _P]),
+    "s2attn_bwd_dq": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _S, _P]),
+    "s2attn_fwd_rope_workspace_size": (_S, [_I, _I, _I, _I, _I]),
+    "s2attn_fwd_rope": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _D, _D, _P, _S, _P]),
+    "s2attn_bwd_rope_workspace_size": (_S, [_I, _I, _I, _I, _I]),
+    "s2attn_bwd_rope": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _D, _D,
+                             _P, _S, _P]),
+    "s2attn_strerror": (ctypes.c_char_p, [_I]),
+    "s2attn_last_error": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+class S2AttnError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"s2attn status {status}: {detail}")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libs2attn.so once; raise if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built; run `python -m grouped_shifted_attention_amd.build` "
+                "(or __graft_entry__.build()) first")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def check(status: int) -> None:
+    if status != S2ATTN_OK:
+        L = lib()
+        detail = L.s2attn_last_error().decode() or L.s2attn_strerror(status).decode()
+        raise S2AttnError(status, detail)

@@ -1,0 +1,345 @@
+// C ABI of the S2-Attn library: argument checks, workspace layout and kernel
+// dispatch.  Every entry point validates all arguments before enqueuing any
+// GPU work and never lets an exception escape.
+#include "s2attn.h"
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <exception>
+#include <string>
+
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const std::string& msg) {
+  g_last_error = msg;
+  return status;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(S2ATTN_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+template <class F>
+int guarded(F&& f) {
+  try {
+    return f();
+  } catch (const std::exception& e) {
+    return fail(S2ATTN_EHIP, std::string("internal error: ") + e.what());
+  } catch (...) {
+    return fail(S2ATTN_EHIP, "internal error");
+  }
+}
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Shape rules.  Returns S2ATTN_OK or an error status (message recorded).
+int check_shape(int B, int N, int H, int Hkv, int D, int G, int shift) {
+  if (B < 0 || N < 0) return fail(S2ATTN_EINVAL, "B and N must be >= 0");
+  if (H < 1 || Hkv < 1) return fail(S2ATTN_EINVAL, "H and Hkv must be >= 1");
+  if (H % Hkv != 0) return fail(S2ATTN_EINVAL, "H must be a multiple of Hkv");
+  if (G < 1) return fail(S2ATTN_EINVAL, "G must be >= 1");
+  if (N % G != 0) return fail(S2ATTN_EINVAL, "N must be a multiple of G");
+  if (shift < 0 || shift >= G) return fail(S2ATTN_EINVAL, "shift must lie in [0, G)");
+  if (shift > 0 && (H % 2 != 0 || Hkv % 2 != 0))
+    return fail(S2ATTN_EINVAL, "with shift > 0, H and Hkv must be even (heads split in halves)");
+  if (D < 1) return fail(S2ATTN_EINVAL, "D must be >= 1");
+  if (D != 64 && D != 128) return fail(S2ATTN_EUNSUPPORTED, "D must be 64 or 128");
+  // Element counts in 64-bit; workgroup counts must fit a 1-D grid.
+  const double elems = (double)B * N * H * D;
+  if (elems > 4.0e18) return fail(S2ATTN_EINVAL, "tensor too large");
+  const double wgs = (double)B * H * ((double)N / G) * ((G + 31) / 32);
+  if (wgs > 2147483647.0) return fail(S2ATTN_EINVAL, "too many work items for one launch");
+  return S2ATTN_OK;
+}
+
+struct Buf {
+  const void* p;
+  size_t bytes;
+  const char* name;
+};
+
+bool overlap(const Buf& a, const Buf& b) {
+  const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+// Null/alignment checks on all buffers and no overlap between any output and
+// any other buffer.
+int check_buffers(const Buf* in, int n_in, const Buf* out, int n_out) {
+  for (int i = 0; i < n_in + n_out; ++i) {
+    const Buf& b = i < n_in ? in[i] : out[i - n_in];
+    if (b.p == nullptr) return fail(S2ATTN_EINVAL, std::string(b.name) + " is NULL");
+    if (((uintptr_t)b.p & 15u) != 0) return fail(S2ATTN_EINVAL, std::string(b.name) + " is not 16-byte aligned");
+  }
+  for (int i = 0; i < n_out; ++i) {
+    for (int j = 0; j < n_in; ++j)
+      if (overlap(out[i], in[j]))
+        return fail(S2ATTN_EINVAL, std::string(out[i].name) + " overlaps " + in[j].name);
+    for (int j = i + 1; j < n_out; ++j)
+      if (overlap(out[i], out[j]))
+        return fail(S2ATTN_EINVAL, std::string(out[i].name) + " overlaps " + out[j].name);
+  }
+  return S2ATTN_OK;
+}
+
+int check_rope(double base, double pos_scale) {
+  if (!std::isfinite(base) || !(base > 0.0)) return fail(S2ATTN_EINVAL, "rope_base must be finite and > 0");
+  if (!std::isfinite(pos_scale) || !(pos_scale > 0.0))
+    return fail(S2ATTN_EINVAL, "pos_scale must be finite and > 0");
+  return S2ATTN_OK;
+}
+
+s2a::RopeTable make_rope(int D, double base, double pos_scale) {
+  s2a::RopeTable t{};
+  const double two_pi = 6.283185307179586;
+  for (int i = 0; i < D / 2; ++i) t.rev[i] = std::pow(base, -2.0 * i / D) / (pos_scale * two_pi);
+  return t;
+}
+
+s2a::Shape make_shape(int B, int N, int H, int Hkv, int D, int G, int shift) {
+  return s2a::Shape{B, N, H, Hkv, D, G, shift, G > 0 ? N / G : 0};
+}
+
+size_t q_bytes(int B, int N, int H, int D) { return (size_t)B * N * H * D * 2; }
+size_t stat_bytes(int B, int N, int H) { return (size_t)B * H * N * 4; }
+
+int do_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int N, int H, int Hkv,
+           int D, int G, int shift, const double* rope, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_shape(B, N, H, Hkv, D, G, shift);
+  if (st) return st;
+  if (rope && (st = check_rope(rope[0], rope[1]))) return st;
+  if (B == 0 || N == 0) return S2ATTN_OK;
+  const size_t qb = q_bytes(B, N, H, D), kb = q_bytes(B, N, Hkv, D);
+  Buf in[3] = {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"}};
+  Buf outs[3] = {{out, qb, "out"}, {nullptr, 0, ""}, {nullptr, 0, ""}};
+  int n_out = 1;
+  if (lse) outs[n_out++] = Buf{lse, stat_bytes(B, N, H), "lse"};
+  if (rope) outs[n_out++] = Buf{ws, round_up(kb), "workspace"};
+  st = check_buffers(in, 3, outs, n_out);
+  if (st) return st;
+  if (rope && ws_bytes < round_up(kb)) return fail(S2ATTN_EINVAL, "workspace too small");
+  if (rope && ((uintptr_t)ws & (kAlign - 1)) != 0) return fail(S2ATTN_EINVAL, "workspace is not 256-byte aligned");
+  const hipStream_t s = (hipStream_t)stream;
+  s2a::FwdArgs a{};
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.out = (uint16_t*)out;
+  a.lse = lse;
+  a.s = make_shape(B, N, H, Hkv, D, G, shift);
+  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
+  hipError_t e;
+  if (rope) {
+    const s2a::RopeTable t = make_rope(D, rope[0], rope[1]);
+    uint16_t* krot = (uint16_t*)ws;
+    if ((e = s2a::launch_rope_rotate(a.k, krot, a.s, Hkv, t, s)) != hipSuccess) return hip_fail(e, "rope(k)");
+    a.k = krot;
+    if ((e = s2a::launch_fwd(a, &t, s)) != hipSuccess) return hip_fail(e, "forward");
+  } else {
+    if ((e = s2a::launch_fwd(a, nullptr, s)) != hipSuccess) return hip_fail(e, "forward");
+  }
+  return S2ATTN_OK;
+}
+
+int do_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse, const void* dout,
+           void* dq, void* dk, void* dv, int B, int N, int H, int Hkv, int D, int G, int shift, const double* rope,
+           void* ws, size_t ws_bytes, void* stream) {
+  int st = check_shape(B, N, H, Hkv, D, G, shift);
+  if (st) return st;
+  if (rope && (st = check_rope(rope[0], rope[1]))) return st;
+  if (B == 0 || N == 0) return S2ATTN_OK;
+  const size_t qb = q_bytes(B, N, H, D), kb = q_bytes(B, N, Hkv, D), sb = stat_bytes(B, N, H);
+  const size_t need = rope ? round_up(sb) + round_up(qb) + round_up(kb) : round_up(sb);
+  Buf in[6] = {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"}, {out, qb, "out"}, {lse, sb, "lse"}, {dout, qb, "dout"}};
+  Buf outs[4] = {{dq, qb, "dq"}, {dk, kb, "dk"}, {dv, kb, "dv"}, {ws, need, "workspace"}};
+  st = check_buffers(in, 6, outs, 4);
+  if (st) return st;
+  if (ws_bytes < need) return fail(S2ATTN_EINVAL, "workspace too small");
+  if (((uintptr_t)ws & (kAlign - 1)) != 0) return fail(S2ATTN_EINVAL, "workspace is not 256-byte aligned");
+  const hipStream_t s = (hipStream_t)stream;
+  char* w = (char*)ws;
+  float* delta = (float*)w;
+  s2a::BwdArgs a{};
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.dout = (const uint16_t*)dout;
+  a.lse = lse;
+  a.delta = delta;
+  a.dq = (uint16_t*)dq;
+  a.dk = (uint16_t*)dk;
+  a.dv = (uint16_t*)dv;
+  a.s = make_shape(B, N, H, Hkv, D, G, shift);
+  a.scale = (float)(1.0 / std::sqrt((double)D));
+  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
+  hipError_t e;
+  s2a::RopeTable t{};
+  if (rope) {
+    t = make_rope(D, rope[0], rope[1]);
+    uint16_t* qrot = (uint16_t*)(w + round_up(sb));
+    uint16_t* krot = (uint16_t*)(w + round_up(sb) + round_up(qb));
+    if ((e = s2a::launch_rope_rotate(a.q, qrot, a.s, H, t, s)) != hipSuccess) return hip_fail(e, "rope(q)");
+    if ((e = s2a::launch_rope_rotate(a.k, krot, a.s, Hkv, t, s)) != hipSuccess) return hip_fail(e, "rope(k)");
+    a.q = qrot;
+    a.k = krot;
+  }
+  if ((e = s2a::launch_bwd_delta((const uint16_t*)out, a.dout, delta, a.s, s)) != hipSuccess)
+    return hip_fail(e, "backward delta");
+  if ((e = s2a::launch_bwd_dkdv(a, rope ? &t : nullptr, s)) != hipSuccess) return hip_fail(e, "backward dk/dv");
+  if ((e = s2a::launch_bwd_dq(a, rope ? &t : nullptr, s)) != hipSuccess) return hip_fail(e, "backward dq");
+  return S2ATTN_OK;
+}
+
+// Stage entry points of the backward (no RoPE).
+enum class Stage { kPre, kDkdv, kDq };
+
+int do_bwd_stage(Stage stage, const void* q, const void* k, const void* v, const void* out, const float* lse,
+                 const void* dout, void* dq, void* dk, void* dv, int B, int N, int H, int Hkv, int D, int G,
+                 int shift, const void* ws, size_t ws_bytes, void* stream) {
+  int st = check_shape(B, N, H, Hkv, D, G, shift);
+  if (st) return st;
+  if (B == 0 || N == 0) return S2ATTN_OK;
+  const size_t qb = q_bytes(B, N, H, D), kb = q_bytes(B, N, Hkv, D), sb = stat_bytes(B, N, H);
+  const size_t need = round_up(sb);
+  if (ws_bytes < need) return fail(S2ATTN_EINVAL, "workspace too small");
+  if (ws == nullptr || ((uintptr_t)ws & (kAlign - 1)) != 0)
+    return fail(S2ATTN_EINVAL, "workspace is NULL or not 256-byte aligned");
+  const hipStream_t s = (hipStream_t)stream;
+  s2a::BwdArgs a{};
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.dout = (const uint16_t*)dout;
+  a.lse = lse;
+  a.delta = (const float*)ws;
+  a.dq = (uint16_t*)dq;
+  a.dk = (uint16_t*)dk;
+  a.dv = (uint16_t*)dv;
+  a.s = make_shape(B, N, H, Hkv, D, G, shift);
+  a.scale = (float)(1.0 / std::sqrt((double)D));
+  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
+  hipError_t e = hipSuccess;
+  if (stage == Stage::kPre) {
+    Buf in[2] = {{out, qb, "out"}, {dout, qb, "dout"}};
+    Buf outs[1] = {{ws, need, "workspace"}};
+    if ((st = check_buffers(in, 2, outs, 1))) return st;
+    e = s2a::launch_bwd_delta((const uint16_t*)out, a.dout, (float*)ws, a.s, s);
+  } else if (stage == Stage::kDkdv) {
+    Buf in[6] = {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"}, {lse, sb, "lse"}, {dout, qb, "dout"},
+                 {ws, need, "workspace"}};
+    Buf outs[2] = {{dk, kb, "dk"}, {dv, kb, "dv"}};
+    if ((st = check_buffers(in, 6, outs, 2))) return st;
+    e = s2a::launch_bwd_dkdv(a, nullptr, s);
+  } else {
+    Buf in[6] = {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"}, {lse, sb, "lse"}, {dout, qb, "dout"},
+                 {ws, need, "workspace"}};
+    Buf outs[1] = {{dq, qb, "dq"}};
+    if ((st = check_buffers(in, 6, outs, 1))) return st;
+    e = s2a::launch_bwd_dq(a, nullptr, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "backward stage");
+  return S2ATTN_OK;
+}
+
+size_t fwd_rope_ws(int B, int N, int H, int Hkv, int D) {
+  if (B <= 0 || N <= 0 || Hkv <= 0 || D <= 0) return 0;
+  (void)H;
+  return round_up(q_bytes(B, N, Hkv, D));
+}
+
+size_t bwd_ws(int B, int N, int H, int Hkv, int D, bool rope) {
+  if (B <= 0 || N <= 0 || H <= 0 || Hkv <= 0 || D <= 0) return 0;
+  size_t n = round_up(stat_bytes(B, N, H));
+  if (rope) n += round_up(q_bytes(B, N, H, D)) + round_up(q_bytes(B, N, Hkv, D));
+  return n;
+}
+
+}  // namespace
+
+extern "C" {
+
+int s2attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int N, int H, int Hkv,
+               int D, int G, int shift, void* stream) {
+  return guarded([&] { return do_fwd(q, k, v, out, lse, B, N, H, Hkv, D, G, shift, nullptr, nullptr, 0, stream); });
+}
+
+size_t s2attn_bwd_workspace_size(int B, int N, int H, int Hkv, int D) { return bwd_ws(B, N, H, Hkv, D, false); }
+
+int s2attn_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse, const void* dout,
+               void* dq, void* dk, void* dv, int B, int N, int H, int Hkv, int D, int G, int shift, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  return guarded([&] {
+    return do_bwd(q, k, v, out, lse, dout, dq, dk, dv, B, N, H, Hkv, D, G, shift, nullptr, workspace,
+                  workspace_bytes, stream);
+  });
+}
+
+int s2attn_bwd_preprocess(const void* out, const void* dout, int B, int N, int H, int D, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return guarded([&] {
+    return do_bwd_stage(Stage::kPre, nullptr, nullptr, nullptr, out, nullptr, dout, nullptr, nullptr, nullptr, B, N,
+                        H, H, D, 1, 0, workspace, workspace_bytes, stream);
+  });
+}
+
+int s2attn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dout, void* dk,
+                    void* dv, int B, int N, int H, int Hkv, int D, int G, int shift, const void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return guarded([&] {
+    return do_bwd_stage(Stage::kDkdv, q, k, v, nullptr, lse, dout, nullptr, dk, dv, B, N, H, Hkv, D, G, shift,
+                        workspace, workspace_bytes, stream);
+  });
+}
+
+int s2attn_bwd_dq(const void* q, const void* k, const void* v, const float* lse, const void* dout, void* dq, int B,
+                  int N, int H, int Hkv, int D, int G, int shift, const void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  return guarded([&] {
+    return do_bwd_stage(Stage::kDq, q, k, v, nullptr, lse, dout, dq, nullptr, nullptr, B, N, H, Hkv, D, G, shift,
+                        workspace, workspace_bytes, stream);
+  });
+}
+
+size_t s2attn_fwd_rope_workspace_size(int B, int N, int H, int Hkv, int D) { return fwd_rope_ws(B, N, H, Hkv, D); }
+
+int s2attn_fwd_rope(const void* q, const void* k, const void* v, void* out, float* lse, int B, int N, int H,
+                    int Hkv, int D, int G, int shift, double rope_base, double pos_scale, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  const double rope[2] = {rope_base, pos_scale};
+  return guarded([&] {
+    return do_fwd(q, k, v, out, lse, B, N, H, Hkv, D, G, shift, rope, workspace, workspace_bytes, stream);
+  });
+}
+
+size_t s2attn_bwd_rope_workspace_size(int B, int N, int H, int Hkv, int D) { return bwd_ws(B, N, H, Hkv, D, true); }
+
+int s2attn_bwd_rope(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                    const void* dout, void* dq, void* dk, void* dv, int B, int N, int H, int Hkv, int D, int G,
+                    int shift, double rope_base, double pos_scale, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  const double rope[2] = {rope_base, pos_scale};
+  return guarded([&] {
+    return do_bwd(q, k, v, out, lse, dout, dq, dk, dv, B, N, H, Hkv, D, G, shift, rope, workspace,
+                  workspace_bytes, stream);
+  });
+}
+
+const char* s2attn_strerror(int status) {
+  switch (status) {
+    case S2ATTN_OK: return "success";
+    case S2ATTN_EINVAL: return "invalid argument";
+    case S2ATTN_EUNSUPPORTED: return "unsupported configuration";
+    case S2ATTN_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* s2attn_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

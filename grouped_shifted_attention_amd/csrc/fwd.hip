@@ -1,0 +1,229 @@
+// S2-Attn forward kernel for gfx950.
+//
+// One workgroup computes BM = 32*NW rows (a "q tile") of one unit (batch b,
+// q head h, group g); wave w owns rows 32w..32w+31 of the tile.  The unit's
+// local row j lives at original position (g*G + j + shift_h) mod N, so the
+// roll by -shift_h and the cut into groups are only address arithmetic
+// (AIMech "LongLoRA and Shifted Sparse Attention (S^2-Attn)", opening
+// definition); the output row is written back to the same original position,
+// which is the roll back by +shift_h.
+//
+// Per k/v tile of BN = 64 keys, staged in LDS (double-buffered, the next
+// tile's global loads in flight during the current tile's math):
+//   S^T = K Q^T           MFMA, A = K rows from LDS, B = Q held in VGPRs
+//   causal mask           only on tiles that cross the wave's diagonal
+//   online softmax        exp2 domain; row max/sum need one lane swap (l^32)
+//   O^T += V^T P^T        MFMA, A = V^T from a transposed LDS tile,
+//                         B = P taken straight from the S^T accumulators
+// Computing S^T (not S) leaves each lane with one query row, so the softmax
+// statistics and the rescale of O are per-lane scalars.
+#include "device_common.hpp"
+#include "kernels.hpp"
+#include "staging.hpp"
+
+namespace s2a {
+
+namespace {
+
+constexpr int kBN = 64;
+
+template <int D, int NW, bool ROPE>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_kernel(FwdArgs a, RopeTable rope) {
+  constexpr int NT = NW * 64;
+  constexpr int BM = NW * 32;
+  using KStage = RowStage<D, kBN, NT>;
+  using VStage = QuadStage<D, kBN, NT>;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kBN * KStage::STR];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VStage::TSTR];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const Shape& s = a.s;
+
+  // Work item: heavy (long causal rows) tiles first within a unit; units
+  // contiguous per XCD.
+  const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
+  const int unit = logical / a.tiles;
+  const int t = a.tiles - 1 - (logical - unit * a.tiles);
+  const int g = unit % s.NG;
+  const int bh = unit / s.NG;
+  const int h = bh % s.H;
+  const int b = bh / s.H;
+  const int sh = (h >= (s.H >> 1)) ? s.shift : 0;
+  const int kvh = h / (s.H / s.Hkv);
+  const int base = g * s.G + sh;
+  const long long kv_row = (long long)s.Hkv * D;
+  const uint16_t* kb_ptr = a.k + (long long)b * s.N * kv_row + (long long)kvh * D;
+  const uint16_t* vb_ptr = a.v + (long long)b * s.N * kv_row + (long long)kvh * D;
+
+  // ---- this lane's query row, held as MFMA B operands ----
+  const int wave_q0 = t * BM + wave * 32;
+  const int qi = wave_q0 + l32;
+  const bool qvalid = qi < s.G;
+  const int qpos = qvalid ? orig_pos(base, qi, s.N) : 0;
+  const long long qoff = ((long long)(b * (long long)s.N + qpos) * s.H + h) * D;
+  bf16x8 qf[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    u32x4 raw = qvalid ? ld16(a.q + qoff + kk * 16 + hh * 8) : zero_u4();
+    if constexpr (ROPE) {
+      float x[8];
+      unpack8(raw, x);
+      rope_rotate8(x, qpos, rope.rev, kk * 16 + hh * 8, false);
+      raw = pack8(x);
+    }
+    qf[kk] = as_bf16x8(raw);
+  }
+
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) o[i] = zero16();
+  float m_run = -INFINITY;  // running max of scaled logits (log2 domain)
+  float l_run = 0.f;        // this lane's half of the running row sum
+
+  const int rows_end = min((t + 1) * BM, s.G);
+  const int ntiles = (rows_end + kBN - 1) / kBN;
+
+  KStage kst;
+  VStage vst;
+  auto load_tile = [&](int n) {
+    const int key0 = n * kBN;
+    kst.load(tid, [&](int row) -> const uint16_t* {
+      const int j = key0 + row;
+      return j < s.G ? kb_ptr + orig_pos(base, j, s.N) * kv_row : nullptr;
+    });
+    vst.load(tid, [&](int row) -> const uint16_t* {
+      const int j = key0 + row;
+      return j < s.G ? vb_ptr + orig_pos(base, j, s.N) * kv_row : nullptr;
+    });
+  };
+  auto store_tile = [&](int buf) {
+    kst.store(tid, Ks[buf]);
+    vst.store(tid, nullptr, Vt[buf]);
+  };
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int n = 0; n < ntiles; ++n) {
+    const int cur = n & 1;
+    if (n + 1 < ntiles) load_tile(n + 1);
+    const int key0 = n * kBN;
+    if (key0 <= wave_q0 + 31) {
+      // S^T = K Q^T: two 32-key blocks.
+      f32x16 sc[kBN / 32];
+#pragma unroll
+      for (int kb = 0; kb < kBN / 32; ++kb) {
+        sc[kb] = zero16();
+        const uint16_t* kp = &Ks[cur][(kb * 32 + l32) * KStage::STR + hh * 8];
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+          sc[kb] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(kp + kk * 16)), qf[kk], sc[kb]);
+      }
+      // Causal mask, only where the tile crosses this wave's diagonal.
+      if (key0 + kBN - 1 > wave_q0) {
+#pragma unroll
+        for (int kb = 0; kb < kBN / 32; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = key0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+            if (j > qi) sc[kb][r] = -INFINITY;
+          }
+      }
+      // Online softmax in the exp2 domain.
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < kBN / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+      mx = half_max(mx);
+      const float m_new = fmaxf(m_run, mx * a.scale_log2);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      float rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < kBN / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(sc[kb][r] * a.scale_log2 - m_new);
+          sc[kb][r] = p;
+          rs += p;
+        }
+      l_run = l_run * alpha + rs;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) o[i] *= alpha;
+      // P as bf16 B operands: accumulator elements 0..7 and 8..15 of each
+      // 32-key block are the two 16-key halves of the reduction.
+      bf16x8 pb[kBN / 32][2];
+#pragma unroll
+      for (int kb = 0; kb < kBN / 32; ++kb) {
+        pb[kb][0] = cvt8(f32x8{sc[kb][0], sc[kb][1], sc[kb][2], sc[kb][3],
+                               sc[kb][4], sc[kb][5], sc[kb][6], sc[kb][7]});
+        pb[kb][1] = cvt8(f32x8{sc[kb][8], sc[kb][9], sc[kb][10], sc[kb][11],
+                               sc[kb][12], sc[kb][13], sc[kb][14], sc[kb][15]});
+      }
+      // O^T += V^T P^T.
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const uint16_t* vp = &Vt[cur][(db * 32 + l32) * VStage::TSTR + hh * 8];
+#pragma unroll
+        for (int kb = 0; kb < kBN / 32; ++kb)
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf)
+            o[db] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(vp + (kb * 2 + hf) * 16)),
+                                 pb[kb][hf], o[db]);
+      }
+    }
+    if (n + 1 < ntiles) store_tile(cur ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: normalise, write O and LSE at the original position ----
+  const float lt = half_sum(l_run);
+  const float inv = 1.f / lt;
+  if (qvalid) {
+    uint16_t* op = a.out + qoff;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d = db * 32 + r4 * 8 + hh * 4;
+        st8(op + d, cvt4_bits(o[db][r4 * 4] * inv, o[db][r4 * 4 + 1] * inv,
+                              o[db][r4 * 4 + 2] * inv, o[db][r4 * 4 + 3] * inv));
+      }
+    if (hh == 0 && a.lse != nullptr)
+      a.lse[((long long)b * s.H + h) * s.N + qpos] = (m_run + __log2f(lt)) * kLn2;
+  }
+}
+
+template <int D, int NW, bool ROPE>
+hipError_t launch_fwd_t(FwdArgs a, const RopeTable* rope, hipStream_t stream) {
+  constexpr int BM = NW * 32;
+  a.tiles = (a.s.G + BM - 1) / BM;
+  const long long grid = (long long)a.s.B * a.s.H * a.s.NG * a.tiles;
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  RopeTable rt{};
+  if (ROPE) rt = *rope;
+  hipLaunchKernelGGL((fwd_kernel<D, NW, ROPE>), dim3((unsigned)grid), dim3(NW * 64), 0, stream, a, rt);
+  return hipGetLastError();
+}
+
+template <int D, bool ROPE>
+hipError_t launch_fwd_d(const FwdArgs& a, const RopeTable* rope, hipStream_t stream) {
+  if (a.s.G <= 64) return launch_fwd_t<D, 2, ROPE>(a, rope, stream);
+  if (a.s.G <= 128) return launch_fwd_t<D, 4, ROPE>(a, rope, stream);
+  return launch_fwd_t<D, 4, ROPE>(a, rope, stream);
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const FwdArgs& a, const RopeTable* rope, hipStream_t stream) {
+  const bool r = rope != nullptr;
+  if (a.s.D == 64) return r ? launch_fwd_d<64, true>(a, rope, stream) : launch_fwd_d<64, false>(a, rope, stream);
+  return r ? launch_fwd_d<128, true>(a, rope, stream) : launch_fwd_d<128, false>(a, rope, stream);
+}
+
+}  // namespace s2a

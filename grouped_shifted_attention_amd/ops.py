@@ -1,0 +1,217 @@
+"""Thin torch-facing binding of the C ABI (include/s2attn.h).
+
+Argument marshalling only: tensors are checked for device, dtype, layout and
+shape, outputs and workspaces are allocated with torch, and the raw device
+pointers plus torch's current HIP stream go to libs2attn.so.  Every step of
+the computation runs in the library's HIP kernels.
+
+Function names match the C entry points.  Tensors: q/out/dout/dq
+[B, N, H, D] bf16, k/v/dk/dv [B, N, Hkv, D] bf16, lse [B, H, N] float32, all
+contiguous on one GPU.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from ._lib import check, lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need(t, name, dtype, shape, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _dims(q, k, v):
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, N, H, D] and k, v [B, N, Hkv, D]")
+    B, N, H, D = q.shape
+    Hkv = k.shape[2]
+    _need(q, "q", torch.bfloat16, (B, N, H, D), None)
+    _need(k, "k", torch.bfloat16, (B, N, Hkv, D), q.device)
+    _need(v, "v", torch.bfloat16, (B, N, Hkv, D), q.device)
+    return B, N, H, Hkv, D
+
+
+def _workspace(nbytes, device):
+    # torch's caching allocator hands out 512-byte aligned blocks.
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def s2attn_fwd(q, k, v, G, shift, out=None, lse=None, with_lse=True):
+    """Forward pass; returns (out, lse) (lse is None when with_lse is False)."""
+    B, N, H, Hkv, D = _dims(q, k, v)
+    out = torch.empty_like(q) if out is None else out
+    _need(out, "out", torch.bfloat16, (B, N, H, D), q.device)
+    if with_lse:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+        _need(lse, "lse", torch.float32, (B, H, N), q.device)
+    else:
+        lse = None
+    check(lib().s2attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                           B, N, H, Hkv, D, int(G), int(shift), _stream(q)))
+    return out, lse
+
+
+def s2attn_fwd_rope(q, k, v, G, shift, rope_base, pos_scale, out=None, lse=None, with_lse=True,
+                    workspace=None):
+    """Forward pass with the fused RoPE + linear position interpolation."""
+    B, N, H, Hkv, D = _dims(q, k, v)
+    out = torch.empty_like(q) if out is None else out
+    _need(out, "out", torch.bfloat16, (B, N, H, D), q.device)
+    if with_lse:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+        _need(lse, "lse", torch.float32, (B, H, N), q.device)
+    else:
+        lse = None
+    L = lib()
+    nbytes = L.s2attn_fwd_rope_workspace_size(B, N, H, Hkv, D)
+    ws = _workspace(nbytes, q.device) if workspace is None else workspace
+    check(L.s2attn_fwd_rope(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                            B, N, H, Hkv, D, int(G), int(shift), float(rope_base), float(pos_scale),
+                            _ptr(ws), ws.numel() * ws.element_size(), _stream(q)))
+    return out, lse
+
+
+def _bwd_common(q, k, v, out, lse, dout, dq, dk, dv):
+    B, N, H, Hkv, D = _dims(q, k, v)
+    _need(out, "out", torch.bfloat16, (B, N, H, D), q.device)
+    _need(dout, "dout", torch.bfloat16, (B, N, H, D), q.device)
+    _need(lse, "lse", torch.float32, (B, H, N), q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _need(dq, "dq", torch.bfloat16, (B, N, H, D), q.device)
+    _need(dk, "dk", torch.bfloat16, (B, N, Hkv, D), q.device)
+    _need(dv, "dv", torch.bfloat16, (B, N, Hkv, D), q.device)
+    return (B, N, H, Hkv, D), dq, dk, dv
+
+
+def s2attn_bwd(q, k, v, out, lse, dout, G, shift, dq=None, dk=None, dv=None, workspace=None):
+    """Backward pass; returns (dq, dk, dv)."""
+    (B, N, H, Hkv, D), dq, dk, dv = _bwd_common(q, k, v, out, lse, dout, dq, dk, dv)
+    L = lib()
+    ws = _workspace(L.s2attn_bwd_workspace_size(B, N, H, Hkv, D), q.device) if workspace is None else workspace
+    check(L.s2attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout),
+                       _ptr(dq), _ptr(dk), _ptr(dv), B, N, H, Hkv, D, int(G), int(shift),
+                       _ptr(ws), ws.numel() * ws.element_size(), _stream(q)))
+    return dq, dk, dv
+
+
+def s2attn_bwd_preprocess(out, dout, workspace):
+    """Stage 1 of the backward: Delta into the workspace."""
+    B, N, H, D = out.shape
+    _need(out, "out", torch.bfloat16, (B, N, H, D), None)
+    _need(dout, "dout", torch.bfloat16, (B, N, H, D), out.device)
+    check(lib().s2attn_bwd_preprocess(_ptr(out), _ptr(dout), B, N, H, D, _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(), _stream(out)))
+
+
+def s2attn_bwd_dkdv(q, k, v, lse, dout, G, shift, workspace, dk=None, dv=None):
+    """Stage 2 of the backward: dk, dv (needs the preprocess stage's workspace)."""
+    B, N, H, Hkv, D = _dims(q, k, v)
+    _need(lse, "lse", torch.float32, (B, H, N), q.device)
+    _need(dout, "dout", torch.bfloat16, (B, N, H, D), q.device)
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _need(dk, "dk", torch.bfloat16, (B, N, Hkv, D), q.device)
+    _need(dv, "dv", torch.bfloat16, (B, N, Hkv, D), q.device)
+    check(lib().s2attn_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dout), _ptr(dk), _ptr(dv),
+                                B, N, H, Hkv, D, int(G), int(shift), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(q)))
+    return dk, dv
+
+
+def s2attn_bwd_dq(q, k, v, lse, dout, G, shift, workspace, dq=None):
+    """Stage 3 of the backward: dq (needs the preprocess stage's workspace)."""
+    B, N, H, Hkv, D = _dims(q, k, v)
+    _need(lse, "lse", torch.float32, (B, H, N), q.device)
+    _need(dout, "dout", torch.bfloat16, (B, N, H, D), q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    _need(dq, "dq", torch.bfloat16, (B, N, H, D), q.device)
+    check(lib().s2attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dout), _ptr(dq),
+                              B, N, H, Hkv, D, int(G), int(shift), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _stream(q)))
+    return dq
+
+
+def s2attn_bwd_rope(q, k, v, out, lse, dout, G, shift, rope_base, pos_scale, dq=None, dk=None, dv=None,
+                    workspace=None):
+    """Backward of s2attn_fwd_rope; dq and dk refer to the unrotated q and k."""
+    (B, N, H, Hkv, D), dq, dk, dv = _bwd_common(q, k, v, out, lse, dout, dq, dk, dv)
+    L = lib()
+    nbytes = L.s2attn_bwd_rope_workspace_size(B, N, H, Hkv, D)
+    ws = _workspace(nbytes, q.device) if workspace is None else workspace
+    check(L.s2attn_bwd_rope(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout),
+                            _ptr(dq), _ptr(dk), _ptr(dv), B, N, H, Hkv, D, int(G), int(shift),
+                            float(rope_base), float(pos_scale),
+                            _ptr(ws), ws.numel() * ws.element_size(), _stream(q)))
+    return dq, dk, dv
+
+
+def bwd_workspace(q, k):
+    """A workspace tensor large enough for s2attn_bwd and its stages."""
+    B, N, H, D = q.shape
+    return _workspace(lib().s2attn_bwd_workspace_size(B, N, H, k.shape[2], D), q.device)
+
+
+def s2attn_workspace_sizes(B, N, H, Hkv, D):
+    """Workspace bytes of the four entry points that take one."""
+    L = lib()
+    return {
+        "bwd": L.s2attn_bwd_workspace_size(B, N, H, Hkv, D),
+        "fwd_rope": L.s2attn_fwd_rope_workspace_size(B, N, H, Hkv, D),
+        "bwd_rope": L.s2attn_bwd_rope_workspace_size(B, N, H, Hkv, D),
+    }
+
+
+class S2AttnFunction(torch.autograd.Function):
+    """Autograd wrapper: forward saves q, k, v, out and lse; backward calls the
+    library's backward entry point."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, G, shift, rope):
+        if rope is None:
+            out, lse = s2attn_fwd(q, k, v, G, shift)
+        else:
+            out, lse = s2attn_fwd_rope(q, k, v, G, shift, rope[0], rope[1])
+        ctx.save_for_backward(q, k, v, out, lse)
+        ctx.cfg = (G, shift, rope)
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, out, lse = ctx.saved_tensors
+        G, shift, rope = ctx.cfg
+        dout = dout.contiguous()
+        if rope is None:
+            dq, dk, dv = s2attn_bwd(q, k, v, out, lse, dout, G, shift)
+        else:
+            dq, dk, dv = s2attn_bwd_rope(q, k, v, out, lse, dout, G, shift, rope[0], rope[1])
+        return dq, dk, dv, None, None, None
+
+
+def s2attn(q, k, v, group_size, shift=None, rope=None):
+    """S2-Attn with autograd.  shift defaults to group_size // 2 (the pages'
+    half-group shift); rope is None or (rope_base, pos_scale)."""
+    shift = group_size // 2 if shift is None else shift
+    return S2AttnFunction.apply(q, k, v, int(group_size), int(shift), rope)

@@ -1,0 +1,145 @@
+/*
+ * s2attn.h - C ABI of the MI355X (gfx950) Shifted Sparse Attention library.
+ *
+ * The operation (AIMech curated page "LongLoRA and Shifted Sparse Attention
+ * (S^2-Attn)", opening definition): projected queries, keys and values are
+ * split along the head axis into two equal halves; the second half is rolled
+ * by -shift along the sequence (the pages use shift = G/2); the sequence is
+ * cut into N/G groups of G tokens; causal softmax attention with logit scale
+ * 1/sqrt(D) runs inside each group only ("LongLoRA: Efficient 100k Context
+ * LLM Fine-Tuning Guide", section "How Shifted Short Attention Works"); the
+ * second half's output is rolled back by +shift.  The roll is circular: the
+ * last group of a shifted head holds the last `shift` tokens followed by the
+ * first `shift` tokens, causal in that rolled order.
+ *
+ * Tensors (all row-major and contiguous, bfloat16 unless stated otherwise):
+ *   q, out, dout, dq : [B, N, H,   D]
+ *   k, v, dk, dv     : [B, N, Hkv, D]
+ *   lse              : [B, H, N] float32, natural-log log-sum-exp of each
+ *                      row's scaled logits, indexed by original position.
+ * Heads h >= H/2 are the shifted half.  Grouped-query sharing: q head h reads
+ * k/v head h / (H/Hkv), rolled by q head h's shift.
+ *
+ * Ownership: every pointer is device memory owned by the caller.  The library
+ * allocates nothing and keeps no pointer after a call returns.  Outputs must
+ * not overlap inputs or each other.  Tensor pointers must be 16-byte aligned.
+ * Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ * null stream); results are ready once the stream is synchronised.
+ *
+ * Errors: every call returns S2ATTN_OK (0) or a negative status and never
+ * throws.  Arguments are checked before any GPU work is enqueued, so a call
+ * that fails with S2ATTN_EINVAL or S2ATTN_EUNSUPPORTED has no effect.
+ * S2ATTN_EHIP reports a HIP launch/runtime error.  Faults during kernel
+ * execution surface at stream synchronisation.  s2attn_last_error() gives a
+ * human-readable detail of the calling thread's most recent failure.
+ * The library holds no global mutable state apart from that per-thread
+ * message; concurrent calls on different streams are safe.
+ *
+ * Accepted shapes: B >= 0, N >= 0, H >= 1, 1 <= Hkv, H % Hkv == 0, G >= 1,
+ * N % G == 0, 0 <= shift < G; with shift > 0, H and Hkv must be even (so the
+ * shifted q heads read exactly the shifted k/v heads).  D must be 64 or 128
+ * (else S2ATTN_EUNSUPPORTED).  B == 0 or N == 0 is a valid empty call.
+ */
+#ifndef S2ATTN_H
+#define S2ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define S2ATTN_OK 0
+#define S2ATTN_EINVAL (-1)
+#define S2ATTN_EUNSUPPORTED (-2)
+#define S2ATTN_EHIP (-3)
+
+/*
+ * Forward pass.  Writes out (and lse unless lse is NULL).
+ * Reads q, k, v; the group split and the rolls are folded into index
+ * arithmetic, nothing is copied.
+ */
+int s2attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+               int B, int N, int H, int Hkv, int D, int G, int shift, void* stream);
+
+/*
+ * Workspace bytes s2attn_bwd needs: the per-row dot products
+ * Delta[b, h, n] = sum_d dout * out (float32, [B, H, N]).
+ */
+size_t s2attn_bwd_workspace_size(int B, int N, int H, int Hkv, int D);
+
+/*
+ * Backward pass: gradients of out w.r.t. q, k, v for the upstream gradient
+ * dout (the calculus of the forward; the pages do not spell it out).
+ * out and lse must be the forward's results for the same q, k, v.
+ * dq, dk, dv are overwritten (not accumulated into).  `workspace` is device
+ * memory of at least s2attn_bwd_workspace_size() bytes (256-byte aligned),
+ * clobbered by the call.  Deterministic: no atomics.
+ */
+int s2attn_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
+               const void* dout, void* dq, void* dk, void* dv,
+               int B, int N, int H, int Hkv, int D, int G, int shift,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The backward in stages: the same kernels s2attn_bwd enqueues, in the same
+ * order, for callers that want to schedule or time them separately.
+ *   s2attn_bwd_preprocess  Delta[b,h,n] = sum_d dout*out into the workspace
+ *   s2attn_bwd_dkdv        dk, dv (reads Delta)
+ *   s2attn_bwd_dq          dq     (reads Delta)
+ * dkdv and dq do not depend on each other and may run on different streams
+ * once preprocess has completed.  Arguments and the workspace are those of
+ * s2attn_bwd (workspace of s2attn_bwd_workspace_size() bytes).
+ */
+int s2attn_bwd_preprocess(const void* out, const void* dout, int B, int N, int H, int D,
+                          void* workspace, size_t workspace_bytes, void* stream);
+int s2attn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
+                    const void* dout, void* dk, void* dv,
+                    int B, int N, int H, int Hkv, int D, int G, int shift,
+                    const void* workspace, size_t workspace_bytes, void* stream);
+int s2attn_bwd_dq(const void* q, const void* k, const void* v, const float* lse,
+                  const void* dout, void* dq,
+                  int B, int N, int H, int Hkv, int D, int G, int shift,
+                  const void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * RoPE with linear position interpolation, fused ahead of the attention
+ * ("LoRA for Long-Context Adaptation", sections "Why vanilla LoRA
+ * under-delivers on long context" and "Position interpolation"): before the
+ * roll, each adjacent pair (x[2i], x[2i+1]) of q and k at original position p
+ * is rotated counter-clockwise by (p / pos_scale) * rope_base^(-2i/D).
+ * q and k are passed unrotated; lse refers to the rotated logits.
+ * rope_base > 0 and pos_scale > 0 must be finite.
+ *
+ * s2attn_fwd_rope needs a workspace for the rotated k ([B, N, Hkv, D] bf16);
+ * q is rotated inside the attention kernel.
+ */
+size_t s2attn_fwd_rope_workspace_size(int B, int N, int H, int Hkv, int D);
+int s2attn_fwd_rope(const void* q, const void* k, const void* v, void* out, float* lse,
+                    int B, int N, int H, int Hkv, int D, int G, int shift,
+                    double rope_base, double pos_scale,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward of s2attn_fwd_rope: dq and dk are gradients w.r.t. the unrotated
+ * q and k (passed back through the transposed rotation).  The workspace holds
+ * Delta plus rotated copies of q and k.
+ */
+size_t s2attn_bwd_rope_workspace_size(int B, int N, int H, int Hkv, int D);
+int s2attn_bwd_rope(const void* q, const void* k, const void* v, const void* out,
+                    const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                    int B, int N, int H, int Hkv, int D, int G, int shift,
+                    double rope_base, double pos_scale,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* s2attn_strerror(int status);
+
+/* Detail of the calling thread's most recent failed call ("" if none). */
+const char* s2attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* S2ATTN_H */

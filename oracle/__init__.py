@@ -23,6 +23,8 @@ from .s2attn_ref import (  # noqa: F401
     s2attn_backward,
     s2attn_unit_forward,
     s2attn_unit_backward,
+    head_unit_forward,
+    head_unit_backward,
     unit_positions,
     dense_causal_attention,
     brute_force_masked_attention,

@@ -292,50 +292,73 @@ def s2attn_backward(q, k, v, dout, G, shift, rope=None):
 # One (batch, head, group) unit, for sampled checks at full size
 # ---------------------------------------------------------------------------
 
-def _unit_operands(q, k, v, dout, G, shift, b, h, g, rope):
-    B, N, H, Hkv, D = _check(q, k, G, shift)
-    sig = head_shift(h, H, shift)
-    kvh = kv_head(h, H, Hkv)
-    qh, kh = q[b, :, h, :], k[b, :, kvh, :]
-    if rope is not None:
-        base, s = rope
-        pos = np.arange(N)
-        qh = rope_rotate(qh, pos, base, s)
-        kh = rope_rotate(kh, pos, base, s)
-    sl = slice(g * G, (g + 1) * G)
-    ops = [roll_sequence(x, -sig)[sl] for x in (qh, kh, v[b, :, kvh, :])]
-    if dout is not None:
-        ops.append(roll_sequence(dout[b, :, h, :], -sig)[sl])
-    return ops, unit_positions(N, G, sig, g), 1.0 / math.sqrt(D)
+def head_unit_forward(qh, kh, vh, G, shift_h, g, rope=None):
+    """One unit from one head's sequences.
 
-
-def s2attn_unit_forward(q, k, v, G, shift, b, h, g, rope=None):
-    """Output rows of one unit (batch b, q head h, group g).
-
-    Returns (positions [G], out [G, D], lse [G]) where ``positions`` are the
-    original sequence positions the rows belong to; these rows equal the
-    matching rows of ``s2attn_forward``.
+    qh is q head h as an [N, D] float64 sequence at original positions, kh and
+    vh the k/v head it reads; shift_h is that head's shift (head_shift()) and
+    g the group.  Applies the optional RoPE at the original positions, rolls
+    by -shift_h, cuts group g out and runs causal attention on it.
+    Returns (positions [G], out [G, D], lse [G]).
     """
-    (qg, kg, vg), pos, scale = _unit_operands(q, k, v, None, G, shift, b, h, g, rope)
+    (qg, kg, vg), pos, scale = _head_unit_operands(qh, kh, vh, None, G, shift_h, g, rope)
     o, lse = group_causal_attention(qg, kg, vg, scale)
     return pos, o, lse
 
 
-def s2attn_unit_backward(q, k, v, dout, G, shift, b, h, g, rope=None):
-    """Gradient contributions of one unit (batch b, q head h, group g).
-
-    Returns (positions [G], dq [G, D], dk [G, D], dv [G, D]).  dq rows are
-    final; dk/dv rows are q head h's share: the full gradient of k/v head
-    kv_head(h) at those positions is the sum over its H/Hkv q heads.  With
-    RoPE, dq and dk are already passed back through the rotation.
-    """
-    (qg, kg, vg, dog), pos, scale = _unit_operands(q, k, v, dout, G, shift, b, h, g, rope)
+def head_unit_backward(qh, kh, vh, doh, G, shift_h, g, rope=None):
+    """Gradient contributions of one unit from one head's sequences (see
+    head_unit_forward); doh is the upstream gradient of q head h's output.
+    Returns (positions [G], dq [G, D], dk [G, D], dv [G, D]); dk/dv are this
+    q head's share of its k/v head's gradient; with RoPE, dq and dk are
+    passed back through the rotation."""
+    (qg, kg, vg, dog), pos, scale = _head_unit_operands(qh, kh, vh, doh, G, shift_h, g, rope)
     dq, dk, dv = group_causal_attention_backward(qg, kg, vg, dog, scale)
     if rope is not None:
         base, s = rope
         dq = rope_rotate(dq, pos, base, s, inverse=True)
         dk = rope_rotate(dk, pos, base, s, inverse=True)
     return pos, dq, dk, dv
+
+
+def _head_unit_operands(qh, kh, vh, doh, G, shift_h, g, rope):
+    N, D = qh.shape
+    if G <= 0 or N % G != 0:
+        raise ValueError("N must be a multiple of G")
+    if rope is not None:
+        base, s = rope
+        pos = np.arange(N)
+        qh = rope_rotate(qh, pos, base, s)
+        kh = rope_rotate(kh, pos, base, s)
+    sl = slice(g * G, (g + 1) * G)
+    ops = [roll_sequence(x, -shift_h)[sl] for x in (qh, kh, vh)]
+    if doh is not None:
+        ops.append(roll_sequence(doh, -shift_h)[sl])
+    return ops, unit_positions(N, G, shift_h, g), 1.0 / math.sqrt(D)
+
+
+def s2attn_unit_forward(q, k, v, G, shift, b, h, g, rope=None):
+    """Output rows of one unit (batch b, q head h, group g) of the whole
+    tensors.  Returns (positions [G], out [G, D], lse [G]) where
+    ``positions`` are the original sequence positions of the rows; these rows
+    equal the matching rows of ``s2attn_forward``."""
+    B, N, H, Hkv, D = _check(q, k, G, shift)
+    kvh = kv_head(h, H, Hkv)
+    return head_unit_forward(q[b, :, h, :], k[b, :, kvh, :], v[b, :, kvh, :], G,
+                             head_shift(h, H, shift), g, rope)
+
+
+def s2attn_unit_backward(q, k, v, dout, G, shift, b, h, g, rope=None):
+    """Gradient contributions of one unit (batch b, q head h, group g) of the
+    whole tensors.  Returns (positions [G], dq [G, D], dk [G, D], dv [G, D]):
+    dq rows are final; dk/dv rows are q head h's share (the full gradient of
+    k/v head kv_head(h) at those positions is the sum over its H/Hkv q
+    heads).  With RoPE, dq and dk are already passed back through the
+    rotation."""
+    B, N, H, Hkv, D = _check(q, k, G, shift)
+    kvh = kv_head(h, H, Hkv)
+    return head_unit_backward(q[b, :, h, :], k[b, :, kvh, :], v[b, :, kvh, :], dout[b, :, h, :], G,
+                              head_shift(h, H, shift), g, rope)
 
 
 # ---------------------------------------------------------------------------

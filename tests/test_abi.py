@@ -1,0 +1,160 @@
+"""CPU tests of the C ABI: the library loads, exports every function that
+include/s2attn.h declares, and rejects bad arguments before touching the GPU.
+
+No call here reaches a kernel launch: every call either fails argument
+validation or is an empty (B == 0 or N == 0) call, both of which return
+before any HIP runtime call.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from grouped_shifted_attention_amd import _lib
+from grouped_shifted_attention_amd.build import LIB_PATH
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "s2attn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB_PATH), reason="libs2attn.so not built")
+
+EINVAL, EUNSUP = _lib.S2ATTN_EINVAL, _lib.S2ATTN_EUNSUPPORTED
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(s2attn_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("s2attn_fwd", "s2attn_bwd", "s2attn_fwd_rope", "s2attn_bwd_rope", "s2attn_strerror"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    handle = ctypes.CDLL(LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(handle, name), name
+    assert set(declared_functions()) == set(_lib.SIGNATURES)
+
+
+def test_status_codes_match_header():
+    text = open(HEADER).read()
+    for name, val in (("S2ATTN_OK", 0), ("S2ATTN_EINVAL", -1), ("S2ATTN_EUNSUPPORTED", -2), ("S2ATTN_EHIP", -3)):
+        m = re.search(rf"#define {name} \(?(-?\d+)\)?", text)
+        assert m and int(m.group(1)) == val
+
+
+def test_strerror():
+    L = _lib.lib()
+    assert L.s2attn_strerror(0) == b"success"
+    assert L.s2attn_strerror(-1) == b"invalid argument"
+    assert L.s2attn_strerror(-2) == b"unsupported configuration"
+    assert L.s2attn_strerror(-3) == b"HIP runtime error"
+    assert L.s2attn_strerror(7) == b"unknown status"
+
+
+FAKE = 0x10000  # 16-byte-aligned non-null address; never dereferenced here
+
+
+def fwd(B=1, N=256, H=4, Hkv=4, D=64, G=64, shift=32, ptrs=None):
+    q = k = v = out = lse = FAKE
+    if ptrs:
+        q, k, v, out, lse = ptrs
+    return _lib.lib().s2attn_fwd(q, k, v, out, lse, B, N, H, Hkv, D, G, shift, None)
+
+
+def detail():
+    return _lib.lib().s2attn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(N=250), "multiple of G"),
+    (dict(G=0), "G must be"),
+    (dict(shift=64), "shift"),
+    (dict(shift=-1), "shift"),
+    (dict(H=3, Hkv=3), "even"),
+    (dict(H=4, Hkv=1), "even"),
+    (dict(H=4, Hkv=3, shift=0), "multiple of Hkv"),
+    (dict(B=-1), ">= 0"),
+    (dict(H=0), ">= 1"),
+    (dict(D=0), "D must be"),
+])
+def test_fwd_rejects_bad_shapes(kw, msg):
+    assert fwd(**kw) == EINVAL
+    assert msg in detail()
+
+
+@pytest.mark.parametrize("D", [32, 96, 256])
+def test_fwd_unsupported_head_dim(D):
+    assert fwd(D=D) == EUNSUP
+
+
+def test_fwd_rejects_null_and_misaligned_pointers():
+    assert fwd(ptrs=(0, FAKE, FAKE, FAKE, FAKE)) == EINVAL and "q is NULL" in detail()
+    assert fwd(ptrs=(FAKE + 2, FAKE, FAKE, FAKE, FAKE)) == EINVAL and "aligned" in detail()
+
+
+def test_fwd_rejects_overlapping_output():
+    q_bytes = 1 * 256 * 4 * 64 * 2
+    base = 0x1000000
+    # out overlaps q
+    assert fwd(ptrs=(base, base + 4 * q_bytes, base + 8 * q_bytes, base + q_bytes - 256, 0)) == EINVAL
+    assert "overlaps" in detail()
+    # lse overlaps out
+    assert fwd(ptrs=(base, base + 4 * q_bytes, base + 8 * q_bytes, base + 12 * q_bytes,
+                     base + 12 * q_bytes + 16)) == EINVAL
+
+
+def test_empty_calls_succeed_without_pointers():
+    L = _lib.lib()
+    assert fwd(B=0, ptrs=(0, 0, 0, 0, 0)) == 0
+    assert fwd(N=0, ptrs=(0, 0, 0, 0, 0)) == 0
+    assert L.s2attn_bwd(None, None, None, None, None, None, None, None, None,
+                        0, 256, 4, 4, 64, 64, 32, None, 0, None) == 0
+    assert L.s2attn_fwd_rope(None, None, None, None, None, 1, 0, 4, 4, 64, 64, 32,
+                             10000.0, 8.0, None, 0, None) == 0
+
+
+def test_bwd_checks_workspace():
+    L = _lib.lib()
+    B, N, H, Hkv, D, G, sh = 1, 256, 4, 4, 64, 64, 32
+    need = L.s2attn_bwd_workspace_size(B, N, H, Hkv, D)
+    assert need >= B * H * N * 4 and need % 256 == 0
+    step = 1 << 24
+    p = [0x10000000 + i * step for i in range(10)]
+    st = L.s2attn_bwd(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7], p[8], B, N, H, Hkv, D, G, sh,
+                      p[9], need - 1, None)
+    assert st == EINVAL and "workspace too small" in detail()
+    st = L.s2attn_bwd(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7], p[8], B, N, H, Hkv, D, G, sh,
+                      p[9] + 16, need, None)
+    assert st == EINVAL and "256-byte" in detail()
+
+
+def test_rope_arguments_are_checked():
+    L = _lib.lib()
+    for base, s in ((0.0, 8.0), (10000.0, 0.0), (float("inf"), 8.0), (10000.0, float("nan"))):
+        st = L.s2attn_fwd_rope(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 256, 4, 4, 64, 64, 32, base, s, FAKE, 1 << 20, None)
+        assert st == EINVAL
+
+
+def test_workspace_sizes():
+    L = _lib.lib()
+    B, N, H, Hkv, D = 1, 32768, 64, 8, 128
+    fr = L.s2attn_fwd_rope_workspace_size(B, N, H, Hkv, D)
+    br = L.s2attn_bwd_rope_workspace_size(B, N, H, Hkv, D)
+    b = L.s2attn_bwd_workspace_size(B, N, H, Hkv, D)
+    assert fr >= B * N * Hkv * D * 2
+    assert b >= B * H * N * 4
+    assert br >= b + B * N * (H + Hkv) * D * 2
+    assert L.s2attn_bwd_workspace_size(0, N, H, Hkv, D) == 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", "/nonexistent/libs2attn.so")
+    with pytest.raises(RuntimeError, match="not built"):
+        _lib.lib()

@@ -41,9 +41,13 @@ def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
     x = np.ascontiguousarray(x, dtype=np.float32)
     if not np.all(np.isfinite(x)):
         raise ValueError("bf16_bits_from_f32: non-finite input")
-    u = x.view(np.uint32).astype(np.uint64)
-    rounding_bias = 0x7FFF + ((u >> 16) & 1)
-    return ((u + rounding_bias) >> 16).astype(np.uint16)
+    u = x.view(np.uint32)
+    # For finite inputs u + 0x8000 stays below 2^32, so uint32 cannot wrap.
+    out = (u >> 16) & 1
+    out += 0x7FFF
+    out += u
+    out >>= 16
+    return out.astype(np.uint16)
 
 
 def f64_from_bf16_bits(bits: np.ndarray) -> np.ndarray:
