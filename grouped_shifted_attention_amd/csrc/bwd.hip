@@ -22,6 +22,8 @@
 #include "kernels.hpp"
 #include "staging.hpp"
 
+#include <type_traits>
+
 namespace s2a {
 
 namespace {
@@ -75,7 +77,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kBN * VStage::STR];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep it scalar
+  const int lane = tid & 63;
   const int l32 = lane & 31, hh = lane >> 5;
   const Shape& s = a.s;
 
@@ -119,72 +122,114 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   VStage vst;
   auto load_tile = [&](int n) {
     const int key0 = n * kBN;
-    kst.load(tid, [&](int row) -> const uint16_t* {
-      const int j = key0 + row;
-      return j < s.G ? kb_ptr + orig_pos(base, j, s.N) * kv_row : nullptr;
-    });
-    vst.load(tid, [&](int row) -> const uint16_t* {
-      const int j = key0 + row;
-      return j < s.G ? vb_ptr + orig_pos(base, j, s.N) * kv_row : nullptr;
-    });
+    const uint16_t* kt = contig_tile(kb_ptr, kv_row, base, key0, kBN, s.G, s.N);
+    if (kt != nullptr) {
+      kst.load_contig(tid, kt, (int)kv_row);
+      vst.load_contig(tid, vb_ptr + (kt - kb_ptr), (int)kv_row);
+    } else {
+      kst.load(tid, [&](int row) -> const uint16_t* {
+        const int j = key0 + row;
+        return j < s.G ? kb_ptr + orig_pos(base, j, s.N) * kv_row : nullptr;
+      });
+      vst.load(tid, [&](int row) -> const uint16_t* {
+        const int j = key0 + row;
+        return j < s.G ? vb_ptr + orig_pos(base, j, s.N) * kv_row : nullptr;
+      });
+    }
   };
   auto store_tile = [&](int buf) {
     kst.store(tid, Ks[buf], Kt[buf]);
     vst.store(tid, Vs[buf]);
   };
 
+  auto compute = [&](int n, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const int cur = n & 1;
+    const int key0 = n * kBN;
+    // S^T = K Q^T and dP^T = V dO^T: four independent accumulator chains,
+    // interleaved; K and V fragments read from LDS one k-step ahead.
+    f32x16 sc[kBN / 32], dp[kBN / 32];
+#pragma unroll
+    for (int kb = 0; kb < kBN / 32; ++kb) {
+      sc[kb] = zero16();
+      dp[kb] = zero16();
+    }
+    {
+      const uint16_t* kp = &Ks[cur][l32 * KStage::STR + hh * 8];
+      const uint16_t* vp = &Vs[cur][l32 * VStage::STR + hh * 8];
+      bf16x8 kf[2][kBN / 32], vf[2][kBN / 32];
+#pragma unroll
+      for (int kb = 0; kb < kBN / 32; ++kb) {
+        kf[0][kb] = lds_frag(kp + kb * 32 * KStage::STR);
+        vf[0][kb] = lds_frag(vp + kb * 32 * VStage::STR);
+      }
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        if (kk + 1 < D / 16) {
+#pragma unroll
+          for (int kb = 0; kb < kBN / 32; ++kb) {
+            kf[(kk + 1) & 1][kb] = lds_frag(kp + kb * 32 * KStage::STR + (kk + 1) * 16);
+            vf[(kk + 1) & 1][kb] = lds_frag(vp + kb * 32 * VStage::STR + (kk + 1) * 16);
+          }
+        }
+#pragma unroll
+        for (int kb = 0; kb < kBN / 32; ++kb) {
+          sc[kb] = mfma32x32x16(kf[kk & 1][kb], qf[kk], sc[kb]);
+          dp[kb] = mfma32x32x16(vf[kk & 1][kb], dof[kk], dp[kb]);
+        }
+      }
+    }
+    bf16x8 dsb[kBN / 32][2];
+#pragma unroll
+    for (int kb = 0; kb < kBN / 32; ++kb) {
+      float ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = fast_exp2(sc[kb][r] * a.scale_log2 - lse2);
+        if constexpr (MASK) {
+          const int j = key0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+          if (j > qi) p = 0.f;
+        }
+        ds[r] = p * (dp[kb][r] - dlt);
+      }
+      dsb[kb][0] = cvt8(f32x8{ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]});
+      dsb[kb][1] = cvt8(f32x8{ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]});
+    }
+    // dQ^T += K^T dS^T: D/32 independent output blocks cycled innermost.
+    {
+      const uint16_t* tp = &Kt[cur][l32 * KStage::TSTR + hh * 8];
+      constexpr int KS = kBN / 16;
+      bf16x8 tf[2][D / 32];
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) tf[0][db] = lds_frag(tp + db * 32 * KStage::TSTR);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + 1 < KS) {
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db)
+            tf[(ks + 1) & 1][db] = lds_frag(tp + db * 32 * KStage::TSTR + (ks + 1) * 16);
+        }
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) dq[db] = mfma32x32x16(tf[ks & 1][db], dsb[ks >> 1][ks & 1], dq[db]);
+      }
+    }
+  };
+
+  auto step = [&](int n, auto mask_tag) {
+    if (n + 1 < ntiles) load_tile(n + 1);
+    compute(n, mask_tag);
+    if (n + 1 < ntiles) store_tile((n & 1) ^ 1);
+    __syncthreads();
+  };
+
   load_tile(0);
   store_tile(0);
   __syncthreads();
 
-  for (int n = 0; n < ntiles; ++n) {
-    const int cur = n & 1;
-    if (n + 1 < ntiles) load_tile(n + 1);
-    const int key0 = n * kBN;
-    if (key0 <= wave_q0 + 31) {
-      f32x16 sc[kBN / 32], dp[kBN / 32];
-#pragma unroll
-      for (int kb = 0; kb < kBN / 32; ++kb) {
-        sc[kb] = zero16();
-        dp[kb] = zero16();
-        const uint16_t* kp = &Ks[cur][(kb * 32 + l32) * KStage::STR + hh * 8];
-        const uint16_t* vp = &Vs[cur][(kb * 32 + l32) * VStage::STR + hh * 8];
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-          sc[kb] = mfma32x32x16(lds_frag(kp + kk * 16), qf[kk], sc[kb]);
-          dp[kb] = mfma32x32x16(lds_frag(vp + kk * 16), dof[kk], dp[kb]);
-        }
-      }
-      const bool diag = key0 + kBN - 1 > wave_q0;
-      bf16x8 dsb[kBN / 32][2];
-#pragma unroll
-      for (int kb = 0; kb < kBN / 32; ++kb) {
-        float ds[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = fast_exp2(sc[kb][r] * a.scale_log2 - lse2);
-          if (diag) {
-            const int j = key0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (j > qi) p = 0.f;
-          }
-          ds[r] = p * (dp[kb][r] - dlt);
-        }
-        dsb[kb][0] = cvt8(f32x8{ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]});
-        dsb[kb][1] = cvt8(f32x8{ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]});
-      }
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const uint16_t* tp = &Kt[cur][(db * 32 + l32) * KStage::TSTR + hh * 8];
-#pragma unroll
-        for (int kb = 0; kb < kBN / 32; ++kb)
-#pragma unroll
-          for (int hf = 0; hf < 2; ++hf)
-            dq[db] = mfma32x32x16(lds_frag(tp + (kb * 2 + hf) * 16), dsb[kb][hf], dq[db]);
-      }
-    }
-    if (n + 1 < ntiles) store_tile(cur ^ 1);
-    __syncthreads();
-  }
+  // Unmasked tiles first, then the diagonal ones (see the forward kernel).
+  const int n_full = min(ntiles, (wave_q0 + 1) / kBN);
+  for (int n = 0; n < n_full; ++n) step(n, std::false_type{});
+  for (int n = n_full; n < ntiles; ++n) step(n, std::true_type{});
 
   if (qvalid) store_row_acc<D, ROPE>(a.dq + qoff, dq, a.scale, hh, qpos, rope);
 }
@@ -209,7 +254,8 @@ __global__ __launch_bounds__(kDkdvWaves * 64) void dkdv_kernel(BwdArgs a, RopeTa
   __shared__ __attribute__((aligned(16))) float Dlt[2][kBMQ];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep it scalar
+  const int lane = tid & 63;
   const int l32 = lane & 31, hh = lane >> 5;
   const Shape& s = a.s;
 
@@ -263,10 +309,15 @@ __global__ __launch_bounds__(kDkdvWaves * 64) void dkdv_kernel(BwdArgs a, RopeTa
     const int i0 = key_start + (step - hi * steps_per_head) * kBMQ;
     const int h = h0 + hi;
     const uint16_t* src = (stage_dout ? a.dout : a.q) + (long long)b * s.N * q_row + (long long)h * D;
-    st.load(stid, [&](int row) -> const uint16_t* {
-      const int i = i0 + row;
-      return i < s.G ? src + orig_pos(base, i, s.N) * q_row : nullptr;
-    });
+    const uint16_t* tile = contig_tile(src, q_row, base, i0, kBMQ, s.G, s.N);
+    if (tile != nullptr) {
+      st.load_contig(stid, tile, (int)q_row);
+    } else {
+      st.load(stid, [&](int row) -> const uint16_t* {
+        const int i = i0 + row;
+        return i < s.G ? src + orig_pos(base, i, s.N) * q_row : nullptr;
+      });
+    }
     if (tid < 2 * kBMQ) {
       const int i = i0 + (tid & (kBMQ - 1));
       const long long so = ((long long)b * s.H + h) * s.N;
@@ -287,63 +338,97 @@ __global__ __launch_bounds__(kDkdvWaves * 64) void dkdv_kernel(BwdArgs a, RopeTa
       Dlt[buf][tid - kBMQ] = stat;
   };
 
+  auto compute = [&](int step, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const int cur = step & 1;
+    const int hi = step / steps_per_head;
+    const int i0 = key_start + (step - hi * steps_per_head) * kBMQ;
+    // S = Q K^T and dP = dO V^T: lane column = this lane's key, elements run
+    // over the step's rows 8*(r/4) + 4*hh + r%4.  Two independent chains,
+    // fragments read one k-step ahead.
+    f32x16 sc = zero16(), dp = zero16();
+    {
+      const uint16_t* qp = &Qs[cur][l32 * Stage::STR + hh * 8];
+      const uint16_t* op = &Os[cur][l32 * Stage::STR + hh * 8];
+      bf16x8 qa[2], oa[2];
+      qa[0] = lds_frag(qp);
+      oa[0] = lds_frag(op);
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        if (kk + 1 < D / 16) {
+          qa[(kk + 1) & 1] = lds_frag(qp + (kk + 1) * 16);
+          oa[(kk + 1) & 1] = lds_frag(op + (kk + 1) * 16);
+        }
+        sc = mfma32x32x16(qa[kk & 1], kf[kk], sc);
+        dp = mfma32x32x16(oa[kk & 1], vf[kk], dp);
+      }
+    }
+    float p[16], ds[16];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int row0 = 8 * r4 + 4 * hh;
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&Lse2[cur][row0]);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&Dlt[cur][row0]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = r4 * 4 + e;
+        float pv = fast_exp2(sc[r] * a.scale_log2 - l4[e]);
+        if constexpr (MASK) {
+          if (kj > i0 + row0 + e) pv = 0.f;
+        }
+        p[r] = pv;
+        ds[r] = pv * (dp[r] - d4[e]);
+      }
+    }
+    bf16x8 pb[2], dsb[2];
+    pb[0] = cvt8(f32x8{p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]});
+    pb[1] = cvt8(f32x8{p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]});
+    dsb[0] = cvt8(f32x8{ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]});
+    dsb[1] = cvt8(f32x8{ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]});
+    // dV^T += dO^T P and dK^T += Q^T dS: 2*D/32 independent accumulators.
+    {
+      const uint16_t* otp = &Ot[cur][l32 * Stage::TSTR + hh * 8];
+      const uint16_t* qtp = &Qt[cur][l32 * Stage::TSTR + hh * 8];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        bf16x8 ofr[D / 32], qfr[D / 32];
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          ofr[db] = lds_frag(otp + db * 32 * Stage::TSTR + hf * 16);
+          qfr[db] = lds_frag(qtp + db * 32 * Stage::TSTR + hf * 16);
+        }
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          dv[db] = mfma32x32x16(ofr[db], pb[hf], dv[db]);
+          dk[db] = mfma32x32x16(qfr[db], dsb[hf], dk[db]);
+        }
+      }
+    }
+  };
+
+  auto do_step = [&](int step, bool active, auto mask_tag) {
+    if (step + 1 < nsteps) load_step(step + 1);
+    if (active) compute(step, mask_tag);
+    if (step + 1 < nsteps) store_step((step & 1) ^ 1);
+    __syncthreads();
+  };
+
   if (nsteps > 0) {
     load_step(0);
     store_step(0);
   }
   __syncthreads();
 
-  for (int step = 0; step < nsteps; ++step) {
-    const int cur = step & 1;
-    if (step + 1 < nsteps) load_step(step + 1);
-    const int hi = step / steps_per_head;
-    const int i0 = key_start + (step - hi * steps_per_head) * kBMQ;
-    if (i0 + kBMQ - 1 >= kw0) {
-      // S = Q K^T and dP = dO V^T: lane column = this lane's key, elements
-      // run over the step's rows 8*(r/4) + 4*hh + r%4.
-      f32x16 sc = zero16(), dp = zero16();
-      const uint16_t* qp = &Qs[cur][l32 * Stage::STR + hh * 8];
-      const uint16_t* op = &Os[cur][l32 * Stage::STR + hh * 8];
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        sc = mfma32x32x16(lds_frag(qp + kk * 16), kf[kk], sc);
-        dp = mfma32x32x16(lds_frag(op + kk * 16), vf[kk], dp);
-      }
-      const bool diag = i0 < kw0 + 31;
-      float p[16], ds[16];
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int row0 = 8 * r4 + 4 * hh;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&Lse2[cur][row0]);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&Dlt[cur][row0]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = r4 * 4 + e;
-          float pv = fast_exp2(sc[r] * a.scale_log2 - l4[e]);
-          if (diag && kj > i0 + row0 + e) pv = 0.f;
-          p[r] = pv;
-          ds[r] = pv * (dp[r] - d4[e]);
-        }
-      }
-      bf16x8 pb[2], dsb[2];
-      pb[0] = cvt8(f32x8{p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]});
-      pb[1] = cvt8(f32x8{p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]});
-      dsb[0] = cvt8(f32x8{ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]});
-      dsb[1] = cvt8(f32x8{ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]});
-      // dV^T += dO^T P,  dK^T += Q^T dS.
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const uint16_t* otp = &Ot[cur][(db * 32 + l32) * Stage::TSTR + hh * 8];
-        const uint16_t* qtp = &Qt[cur][(db * 32 + l32) * Stage::TSTR + hh * 8];
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          dv[db] = mfma32x32x16(lds_frag(otp + hf * 16), pb[hf], dv[db]);
-          dk[db] = mfma32x32x16(lds_frag(qtp + hf * 16), dsb[hf], dk[db]);
-        }
-      }
-    }
-    if (step + 1 < nsteps) store_step(cur ^ 1);
-    __syncthreads();
+  // Per q head: steps whose rows all precede this wave's keys are skipped,
+  // steps crossing the diagonal are masked, the rest run unmasked.  The step
+  // sequence (and so the barrier count) is the same for every wave.
+  const int skip = min(steps_per_head, (kw0 - key_start) / kBMQ);   // rows < kw0 only
+  const int diag_end = min(steps_per_head, (kw0 + 31 - key_start) / kBMQ + 1);
+  for (int hi = 0; hi < rq; ++hi) {
+    const int s0 = hi * steps_per_head;
+    for (int j = 0; j < skip; ++j) do_step(s0 + j, false, std::false_type{});
+    for (int j = skip; j < diag_end; ++j) do_step(s0 + j, true, std::true_type{});
+    for (int j = diag_end; j < steps_per_head; ++j) do_step(s0 + j, true, std::false_type{});
   }
 
   if (kvalid) {

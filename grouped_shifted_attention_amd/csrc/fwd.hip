@@ -21,11 +21,14 @@
 #include "kernels.hpp"
 #include "staging.hpp"
 
+#include <type_traits>
+
 namespace s2a {
 
 namespace {
 
 constexpr int kBN = 64;
+constexpr float kLazy = 8.f;  // log2-domain slack before the softmax reference moves
 
 template <int D, int NW, bool ROPE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_kernel(FwdArgs a, RopeTable rope) {
@@ -37,7 +40,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VStage::TSTR];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep it scalar
+  const int lane = tid & 63;
   const int l32 = lane & 31, hh = lane >> 5;
   const Shape& s = a.s;
 
@@ -89,96 +93,141 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   VStage vst;
   auto load_tile = [&](int n) {
     const int key0 = n * kBN;
-    kst.load(tid, [&](int row) -> const uint16_t* {
-      const int j = key0 + row;
-      return j < s.G ? kb_ptr + orig_pos(base, j, s.N) * kv_row : nullptr;
-    });
-    vst.load(tid, [&](int row) -> const uint16_t* {
-      const int j = key0 + row;
-      return j < s.G ? vb_ptr + orig_pos(base, j, s.N) * kv_row : nullptr;
-    });
+    const uint16_t* kt = contig_tile(kb_ptr, kv_row, base, key0, kBN, s.G, s.N);
+    if (kt != nullptr) {
+      kst.load_contig(tid, kt, (int)kv_row);
+      vst.load_contig(tid, vb_ptr + (kt - kb_ptr), (int)kv_row);
+    } else {
+      kst.load(tid, [&](int row) -> const uint16_t* {
+        const int j = key0 + row;
+        return j < s.G ? kb_ptr + orig_pos(base, j, s.N) * kv_row : nullptr;
+      });
+      vst.load(tid, [&](int row) -> const uint16_t* {
+        const int j = key0 + row;
+        return j < s.G ? vb_ptr + orig_pos(base, j, s.N) * kv_row : nullptr;
+      });
+    }
   };
   auto store_tile = [&](int buf) {
     kst.store(tid, Ks[buf]);
     vst.store(tid, nullptr, Vt[buf]);
   };
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int n = 0; n < ntiles; ++n) {
+  // One k/v tile: S^T = K Q^T, online softmax, O^T += V^T P^T.  MASK is set
+  // only for tiles that reach past this wave's first row (the diagonal).
+  auto compute = [&](int n, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int cur = n & 1;
-    if (n + 1 < ntiles) load_tile(n + 1);
     const int key0 = n * kBN;
-    if (key0 <= wave_q0 + 31) {
-      // S^T = K Q^T: two 32-key blocks.
-      f32x16 sc[kBN / 32];
+    // S^T: the two 32-key blocks are independent accumulators, interleaved
+    // so back-to-back MFMAs never wait on each other; K fragments are read
+    // from LDS one k-step ahead.
+    f32x16 sc[kBN / 32];
 #pragma unroll
-      for (int kb = 0; kb < kBN / 32; ++kb) {
-        sc[kb] = zero16();
-        const uint16_t* kp = &Ks[cur][(kb * 32 + l32) * KStage::STR + hh * 8];
+    for (int kb = 0; kb < kBN / 32; ++kb) sc[kb] = zero16();
+    {
+      const uint16_t* kp = &Ks[cur][l32 * KStage::STR + hh * 8];
+      bf16x8 kf[2][kBN / 32];
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk)
-          sc[kb] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(kp + kk * 16)), qf[kk], sc[kb]);
+      for (int kb = 0; kb < kBN / 32; ++kb) kf[0][kb] = lds_frag(kp + kb * 32 * KStage::STR);
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        if (kk + 1 < D / 16) {
+#pragma unroll
+          for (int kb = 0; kb < kBN / 32; ++kb)
+            kf[(kk + 1) & 1][kb] = lds_frag(kp + kb * 32 * KStage::STR + (kk + 1) * 16);
+        }
+#pragma unroll
+        for (int kb = 0; kb < kBN / 32; ++kb) sc[kb] = mfma32x32x16(kf[kk & 1][kb], qf[kk], sc[kb]);
       }
-      // Causal mask, only where the tile crosses this wave's diagonal.
-      if (key0 + kBN - 1 > wave_q0) {
-#pragma unroll
-        for (int kb = 0; kb < kBN / 32; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j = key0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (j > qi) sc[kb][r] = -INFINITY;
-          }
-      }
-      // Online softmax in the exp2 domain.
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < kBN / 32; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
-      mx = half_max(mx);
-      const float m_new = fmaxf(m_run, mx * a.scale_log2);
-      const float alpha = fast_exp2(m_run - m_new);
-      m_run = m_new;
-      float rs = 0.f;
+    }
+    if constexpr (MASK) {
 #pragma unroll
       for (int kb = 0; kb < kBN / 32; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(sc[kb][r] * a.scale_log2 - m_new);
-          sc[kb][r] = p;
-          rs += p;
+          const int j = key0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+          if (j > qi) sc[kb][r] = -INFINITY;
         }
-      l_run = l_run * alpha + rs;
+    }
+    // Online softmax in the exp2 domain with a lazily moved reference: the
+    // accumulators are rescaled only when some row's max exceeds the current
+    // reference by more than kLazy (so p <= 2^kLazy); otherwise the stale
+    // reference stays, which changes nothing in exact arithmetic.
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < kBN / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+    mx = half_max(mx) * a.scale_log2;
+    if (__any(mx > m_run + kLazy)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < D / 32; ++i) o[i] *= alpha;
-      // P as bf16 B operands: accumulator elements 0..7 and 8..15 of each
-      // 32-key block are the two 16-key halves of the reduction.
-      bf16x8 pb[kBN / 32][2];
+    }
+    float rs = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < kBN / 32; ++kb) {
-        pb[kb][0] = cvt8(f32x8{sc[kb][0], sc[kb][1], sc[kb][2], sc[kb][3],
-                               sc[kb][4], sc[kb][5], sc[kb][6], sc[kb][7]});
-        pb[kb][1] = cvt8(f32x8{sc[kb][8], sc[kb][9], sc[kb][10], sc[kb][11],
-                               sc[kb][12], sc[kb][13], sc[kb][14], sc[kb][15]});
+    for (int kb = 0; kb < kBN / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pv = fast_exp2(sc[kb][r] * a.scale_log2 - m_run);
+        sc[kb][r] = pv;
+        rs += pv;
       }
-      // O^T += V^T P^T.
+    l_run += rs;
+    // P as bf16 B operands: accumulator elements 0..7 and 8..15 of each
+    // 32-key block are the two 16-key halves of the reduction.
+    bf16x8 pb[kBN / 32][2];
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const uint16_t* vp = &Vt[cur][(db * 32 + l32) * VStage::TSTR + hh * 8];
+    for (int kb = 0; kb < kBN / 32; ++kb) {
+      pb[kb][0] = cvt8(f32x8{sc[kb][0], sc[kb][1], sc[kb][2], sc[kb][3],
+                             sc[kb][4], sc[kb][5], sc[kb][6], sc[kb][7]});
+      pb[kb][1] = cvt8(f32x8{sc[kb][8], sc[kb][9], sc[kb][10], sc[kb][11],
+                             sc[kb][12], sc[kb][13], sc[kb][14], sc[kb][15]});
+    }
+    // O^T += V^T P^T: the D/32 output blocks are independent accumulators,
+    // cycled in the inner loop; V^T fragments are read one step ahead.
+    {
+      const uint16_t* vp = &Vt[cur][l32 * VStage::TSTR + hh * 8];
+      constexpr int KS = kBN / 16;  // 16-key reduction steps per tile
+      bf16x8 vf[2][D / 32];
 #pragma unroll
-        for (int kb = 0; kb < kBN / 32; ++kb)
+      for (int db = 0; db < D / 32; ++db) vf[0][db] = lds_frag(vp + db * 32 * VStage::TSTR);
 #pragma unroll
-          for (int hf = 0; hf < 2; ++hf)
-            o[db] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(vp + (kb * 2 + hf) * 16)),
-                                 pb[kb][hf], o[db]);
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + 1 < KS) {
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db)
+            vf[(ks + 1) & 1][db] = lds_frag(vp + db * 32 * VStage::TSTR + (ks + 1) * 16);
+        }
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+          o[db] = mfma32x32x16(vf[ks & 1][db], pb[ks >> 1][ks & 1], o[db]);
       }
     }
-    if (n + 1 < ntiles) store_tile(cur ^ 1);
+  };
+
+  auto step = [&](int n, auto mask_tag) {
+    if (n + 1 < ntiles) load_tile(n + 1);
+    compute(n, mask_tag);
+    if (n + 1 < ntiles) store_tile((n & 1) ^ 1);
     __syncthreads();
-  }
+  };
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  // Tiles whose keys all precede this wave's first row need no mask; the
+  // rest (the diagonal, and for the lower waves of the tile one tile wholly
+  // above them, which the mask zeroes) do.  Every wave runs ntiles steps, so
+  // the barriers match.
+  const int n_full = min(ntiles, (wave_q0 + 1) / kBN);
+  for (int n = 0; n < n_full; ++n) step(n, std::false_type{});
+  for (int n = n_full; n < ntiles; ++n) step(n, std::true_type{});
 
   // ---- epilogue: normalise, write O and LSE at the original position ----
   const float lt = half_sum(l_run);

@@ -47,6 +47,21 @@ struct RowStage {
     }
   }
 
+  // Fast path: the R rows are consecutive rows of the tensor starting at
+  // `tile0` (no group end, no wrap inside the tile), `row_stride` elements
+  // apart.  The per-thread offset is loop-invariant, so each load is one
+  // instruction off a uniform base.
+  __device__ __forceinline__ void load_contig(int tid, const uint16_t* tile0, int row_stride) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int item = tid + i * NT;
+      if (ITEMS % NT == 0 || item < ITEMS) {
+        const int row = item / CH, ch = item % CH;
+        r[i] = ld16(tile0 + (row * row_stride + ch * 8));
+      }
+    }
+  }
+
   __device__ __forceinline__ void store(int tid, uint16_t* lds) const {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
@@ -89,6 +104,20 @@ struct QuadStage {
     }
   }
 
+  // Fast path for R consecutive rows starting at `tile0` (see RowStage).
+  __device__ __forceinline__ void load_contig(int tid, const uint16_t* tile0, int row_stride) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int item = tid + i * NT;
+      if (ITEMS % NT == 0 || item < ITEMS) {
+        const int rq = item % NQ, oc = item / NQ;
+        const int off = rq * 4 * row_stride + oc * 8;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) r[i][u] = ld16(tile0 + u * row_stride + off);
+      }
+    }
+  }
+
   // row_lds may be nullptr (transposed copy only).
   __device__ __forceinline__ void store(int tid, uint16_t* row_lds, uint16_t* tr_lds) const {
 #pragma unroll
@@ -119,6 +148,18 @@ struct QuadStage {
     }
   }
 };
+
+// Start of a tile of R local rows beginning at local row j0 of a group whose
+// first rolled row is at original position `base`, if those R rows are R
+// consecutive original positions inside the group; nullptr otherwise (the
+// tile reaches past the group end or wraps around the sequence end).
+__device__ __forceinline__ const uint16_t* contig_tile(const uint16_t* head0, long long row_stride, int base,
+                                                       int j0, int R, int G, int N) {
+  if (j0 + R > G) return nullptr;
+  const int p0 = base + j0;
+  if (p0 < N && p0 + R > N) return nullptr;
+  return head0 + (long long)(p0 >= N ? p0 - N : p0) * row_stride;
+}
 
 // 16-byte LDS read as an MFMA operand.
 __device__ __forceinline__ bf16x8 lds_frag(const uint16_t* p) {
