@@ -14,7 +14,8 @@
 //                each wave owns 32 keys, keeps K and V as MFMA B operands in
 //                VGPRs and accumulates dK^T, dV^T over every q head sharing
 //                the k/v head and every 32-row q step from the diagonal to
-//                the group end.  4 MFMA products per step.
+//                the group end.  4 MFMA products per step; Q^T and dO^T are
+//                read transposed (ds_read_b64_tr_b16) from row-major tiles.
 //   dq_kernel    one workgroup per (batch, q head, group, q tile); each wave
 //                owns 32 query rows and walks the k/v tiles up to the
 //                diagonal.  3 MFMA products per tile.
@@ -68,18 +69,16 @@ __device__ __forceinline__ void store_row_acc(uint16_t* row_ptr, const f32x16* a
 template <int D, int NW, bool ROPE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void dq_kernel(BwdArgs a,
                                                                                                  RopeTable rope) {
-  constexpr int NT = NW * 64;
   constexpr int BM = NW * 32;
-  using KStage = QuadStage<D, kBN, NT>;  // row-major (S^T) + transposed (dQ^T)
-  using VStage = RowStage<D, kBN, NT>;   // row-major (dP^T)
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kBN * KStage::STR];
-  __shared__ __attribute__((aligned(16))) uint16_t Kt[2][D * KStage::TSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kBN * VStage::STR];
+  using TileStage = LdsStage<D, kBN, NW>;  // K rows (S^T; read transposed for dQ^T), V rows (dP^T)
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kBN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kBN * D];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep it scalar
   const int lane = tid & 63;
   const int l32 = lane & 31, hh = lane >> 5;
+  const SwzLane<D> sw(lane);
   const Shape& s = a.s;
 
   const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
@@ -118,99 +117,72 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int rows_end = min((t + 1) * BM, s.G);
   const int ntiles = (rows_end + kBN - 1) / kBN;
 
-  KStage kst;
-  VStage vst;
+  const TileStage ts(wave, lane, (int)kv_row);
   auto load_tile = [&](int n) {
     const int key0 = n * kBN;
+    const int buf = n & 1;
     const uint16_t* kt = contig_tile(kb_ptr, kv_row, base, key0, kBN, s.G, s.N);
     if (kt != nullptr) {
-      kst.load_contig(tid, kt, (int)kv_row);
-      vst.load_contig(tid, vb_ptr + (kt - kb_ptr), (int)kv_row);
+      ts.load_contig(kt, Ks[buf], wave);
+      ts.load_contig(vb_ptr + (kt - kb_ptr), Vs[buf], wave);
     } else {
-      kst.load(tid, [&](int row) -> const uint16_t* {
-        const int j = key0 + row;
-        return j < s.G ? kb_ptr + orig_pos(base, j, s.N) * kv_row : nullptr;
-      });
-      vst.load(tid, [&](int row) -> const uint16_t* {
-        const int j = key0 + row;
-        return j < s.G ? vb_ptr + orig_pos(base, j, s.N) * kv_row : nullptr;
-      });
+      auto rows = [&](const uint16_t* head0) {
+        return [=, &s](int row) {
+          const int j = min(key0 + row, s.G - 1);
+          return head0 + orig_pos(base, j, s.N) * kv_row;
+        };
+      };
+      ts.load_rows(rows(kb_ptr), Ks[buf], wave, lane);
+      ts.load_rows(rows(vb_ptr), Vs[buf], wave, lane);
     }
-  };
-  auto store_tile = [&](int buf) {
-    kst.store(tid, Ks[buf], Kt[buf]);
-    vst.store(tid, Vs[buf]);
   };
 
   auto compute = [&](int n, auto mask_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const int cur = n & 1;
     const int key0 = n * kBN;
-    // S^T = K Q^T and dP^T = V dO^T: four independent accumulator chains,
-    // interleaved; K and V fragments read from LDS one k-step ahead.
-    f32x16 sc[kBN / 32], dp[kBN / 32];
+    // Two 32-key halves in turn (keeps the live S/dP set small enough for
+    // two waves per SIMD).  Per half: S^T = K Q^T and dP^T = V dO^T (two
+    // accumulators, K/V fragments read one k-step ahead), P and dS on the
+    // VALU, then dQ^T += K^T dS^T with K^T read transposed from the
+    // row-major K tile.
 #pragma unroll
     for (int kb = 0; kb < kBN / 32; ++kb) {
-      sc[kb] = zero16();
-      dp[kb] = zero16();
-    }
-    {
-      const uint16_t* kp = &Ks[cur][l32 * KStage::STR + hh * 8];
-      const uint16_t* vp = &Vs[cur][l32 * VStage::STR + hh * 8];
-      bf16x8 kf[2][kBN / 32], vf[2][kBN / 32];
+      f32x16 sc = zero16(), dp = zero16();
+      {
+        bf16x8 kf[2], vf[2];
+        kf[0] = sw.row(Ks[cur], kb * 32, 0);
+        vf[0] = sw.row(Vs[cur], kb * 32, 0);
 #pragma unroll
-      for (int kb = 0; kb < kBN / 32; ++kb) {
-        kf[0][kb] = lds_frag(kp + kb * 32 * KStage::STR);
-        vf[0][kb] = lds_frag(vp + kb * 32 * VStage::STR);
-      }
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        if (kk + 1 < D / 16) {
-#pragma unroll
-          for (int kb = 0; kb < kBN / 32; ++kb) {
-            kf[(kk + 1) & 1][kb] = lds_frag(kp + kb * 32 * KStage::STR + (kk + 1) * 16);
-            vf[(kk + 1) & 1][kb] = lds_frag(vp + kb * 32 * VStage::STR + (kk + 1) * 16);
+        for (int kk = 0; kk < D / 16; ++kk) {
+          if (kk + 1 < D / 16) {
+            kf[(kk + 1) & 1] = sw.row(Ks[cur], kb * 32, kk + 1);
+            vf[(kk + 1) & 1] = sw.row(Vs[cur], kb * 32, kk + 1);
           }
-        }
-#pragma unroll
-        for (int kb = 0; kb < kBN / 32; ++kb) {
-          sc[kb] = mfma32x32x16(kf[kk & 1][kb], qf[kk], sc[kb]);
-          dp[kb] = mfma32x32x16(vf[kk & 1][kb], dof[kk], dp[kb]);
+          sc = mfma32x32x16(kf[kk & 1], qf[kk], sc);
+          dp = mfma32x32x16(vf[kk & 1], dof[kk], dp);
         }
       }
-    }
-    bf16x8 dsb[kBN / 32][2];
-#pragma unroll
-    for (int kb = 0; kb < kBN / 32; ++kb) {
       float ds[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float p = fast_exp2(sc[kb][r] * a.scale_log2 - lse2);
+        float p = fast_exp2(sc[r] * a.scale_log2 - lse2);
         if constexpr (MASK) {
           const int j = key0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
           if (j > qi) p = 0.f;
         }
-        ds[r] = p * (dp[kb][r] - dlt);
+        ds[r] = p * (dp[r] - dlt);
       }
-      dsb[kb][0] = cvt8(f32x8{ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]});
-      dsb[kb][1] = cvt8(f32x8{ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]});
-    }
-    // dQ^T += K^T dS^T: D/32 independent output blocks cycled innermost.
-    {
-      const uint16_t* tp = &Kt[cur][l32 * KStage::TSTR + hh * 8];
-      constexpr int KS = kBN / 16;
-      bf16x8 tf[2][D / 32];
+      bf16x8 dsb[2];
+      dsb[0] = cvt8(f32x8{ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]});
+      dsb[1] = cvt8(f32x8{ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]});
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) tf[0][db] = lds_frag(tp + db * 32 * KStage::TSTR);
+      for (int hf = 0; hf < 2; ++hf) {
+        bf16x8 tf[D / 32];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        if (ks + 1 < KS) {
+        for (int db = 0; db < D / 32; ++db) tf[db] = sw.tr(Ks[cur], kb * 32 + hf * 16, db);
 #pragma unroll
-          for (int db = 0; db < D / 32; ++db)
-            tf[(ks + 1) & 1][db] = lds_frag(tp + db * 32 * KStage::TSTR + (ks + 1) * 16);
-        }
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) dq[db] = mfma32x32x16(tf[ks & 1][db], dsb[ks >> 1][ks & 1], dq[db]);
+        for (int db = 0; db < D / 32; ++db) dq[db] = mfma32x32x16(tf[db], dsb[hf], dq[db]);
       }
     }
   };
@@ -218,12 +190,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   auto step = [&](int n, auto mask_tag) {
     if (n + 1 < ntiles) load_tile(n + 1);
     compute(n, mask_tag);
-    if (n + 1 < ntiles) store_tile((n & 1) ^ 1);
+    wait_vmem_all();
     __syncthreads();
   };
 
   load_tile(0);
-  store_tile(0);
+  wait_vmem_all();
   __syncthreads();
 
   // Unmasked tiles first, then the diagonal ones (see the forward kernel).
@@ -237,26 +209,38 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 // ---------------------------------------------------------------------------
 // dK, dV
 // ---------------------------------------------------------------------------
-constexpr int kDkdvWaves = 4;
-constexpr int kBNK = kDkdvWaves * 32;  // keys per workgroup
+// Eight waves per workgroup, two per SIMD, specialised in pairs that share
+// 32 keys: the "P wave" (waves 0-3) computes S = Q K^T, P and dV^T += dO^T P
+// and publishes its bf16 P through LDS; the "dS wave" (waves 4-7) runs one
+// step behind on the same keys and computes dP = dO V^T, dS = P (dP - Delta)
+// and dK^T += Q^T dS.  Each keeps one of K/V and one of dK/dV, which halves
+// the registers a wave needs against one wave doing all four products.
+// q/dout tiles are triple-buffered so that step n+1 stages while the two
+// roles work on steps n and n-1; one barrier per step.
+constexpr int kDkdvPairs = 4;
+constexpr int kDkdvWaves = 2 * kDkdvPairs;
+constexpr int kBNK = kDkdvPairs * 32;  // keys per workgroup
 constexpr int kBMQ = 32;               // q rows per step
+constexpr int kStages = 3;
 
 template <int D, bool ROPE>
-__global__ __launch_bounds__(kDkdvWaves * 64) void dkdv_kernel(BwdArgs a, RopeTable rope) {
-  constexpr int NT = kDkdvWaves * 64;
-  // Threads [0, NT/2) stage the q rows of a step, [NT/2, NT) the dout rows.
-  using Stage = QuadStage<D, kBMQ, NT / 2>;
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][kBMQ * Stage::STR];
-  __shared__ __attribute__((aligned(16))) uint16_t Qt[2][D * Stage::TSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t Os[2][kBMQ * Stage::STR];
-  __shared__ __attribute__((aligned(16))) uint16_t Ot[2][D * Stage::TSTR];
-  __shared__ __attribute__((aligned(16))) float Lse2[2][kBMQ];
-  __shared__ __attribute__((aligned(16))) float Dlt[2][kBMQ];
+__global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void dkdv_kernel(
+    BwdArgs a, RopeTable rope) {
+  using TileStage = LdsStage<D, kBMQ, kDkdvWaves>;
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[kStages][kBMQ * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Os[kStages][kBMQ * D];
+  __shared__ __attribute__((aligned(16))) float Lse2[kStages][kBMQ];
+  __shared__ __attribute__((aligned(16))) float Dlt[kStages][kBMQ];
+  // P hand-over: [buffer][pair][half][lane] 16 bytes (8 bf16).
+  __shared__ __attribute__((aligned(16))) u32x4 Pbuf[2][kDkdvPairs][2][64];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep it scalar
   const int lane = tid & 63;
   const int l32 = lane & 31, hh = lane >> 5;
+  const SwzLane<D> sw(lane);
+  const bool ds_wave = wave >= kDkdvPairs;
+  const int pair = wave & (kDkdvPairs - 1);
   const Shape& s = a.s;
 
   // Work item: (b, kv head, group) units, key tiles with the most rows first.
@@ -274,49 +258,51 @@ __global__ __launch_bounds__(kDkdvWaves * 64) void dkdv_kernel(BwdArgs a, RopeTa
   const long long kv_row = (long long)s.Hkv * D;
   const long long q_row = (long long)s.H * D;
 
-  // This lane's key: K and V rows as MFMA B operands.
+  // This lane's key; the P wave holds K, the dS wave V, as MFMA B operands.
   const int key_start = tk * kBNK;
-  const int kw0 = key_start + wave * 32;
+  const int kw0 = key_start + pair * 32;
   const int kj = kw0 + l32;
   const bool kvalid = kj < s.G;
   const int kpos = kvalid ? orig_pos(base, kj, s.N) : 0;
   const long long koff = ((long long)b * s.N + kpos) * kv_row + (long long)kvh * D;
-  bf16x8 kf[D / 16], vf[D / 16];
+  const uint16_t* kv_src = ds_wave ? a.v : a.k;
+  bf16x8 kvf[D / 16];
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    kf[kk] = as_bf16x8(kvalid ? ld16(a.k + koff + kk * 16 + hh * 8) : zero_u4());
-    vf[kk] = as_bf16x8(kvalid ? ld16(a.v + koff + kk * 16 + hh * 8) : zero_u4());
-  }
+  for (int kk = 0; kk < D / 16; ++kk)
+    kvf[kk] = as_bf16x8(kvalid ? ld16(kv_src + koff + kk * 16 + hh * 8) : zero_u4());
 
-  f32x16 dk[D / 32], dv[D / 32];
+  f32x16 acc[D / 32];  // dV^T (P wave) or dK^T (dS wave)
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i) {
-    dk[i] = zero16();
-    dv[i] = zero16();
-  }
+  for (int i = 0; i < D / 32; ++i) acc[i] = zero16();
 
   // Steps: every q head sharing this k/v head x every 32-row block from the
   // first row that can see this tile's keys to the group end.
   const int steps_per_head = (s.G - key_start + kBMQ - 1) / kBMQ;
   const int nsteps = steps_per_head * rq;
 
-  const bool stage_dout = tid >= NT / 2;
-  const int stid = tid & (NT / 2 - 1);
-  Stage st;
+  const TileStage ts(wave, lane, (int)q_row);
   float stat = 0.f;
+  // q and dout rows of a step go straight into LDS; rows past the group end
+  // point at the group's last row (their P is exactly zero: lse = +inf).
   auto load_step = [&](int step) {
     const int hi = step / steps_per_head;
     const int i0 = key_start + (step - hi * steps_per_head) * kBMQ;
     const int h = h0 + hi;
-    const uint16_t* src = (stage_dout ? a.dout : a.q) + (long long)b * s.N * q_row + (long long)h * D;
-    const uint16_t* tile = contig_tile(src, q_row, base, i0, kBMQ, s.G, s.N);
-    if (tile != nullptr) {
-      st.load_contig(stid, tile, (int)q_row);
+    const int buf = step % kStages;
+    const long long head_off = (long long)b * s.N * q_row + (long long)h * D;
+    const uint16_t* qt = contig_tile(a.q + head_off, q_row, base, i0, kBMQ, s.G, s.N);
+    if (qt != nullptr) {
+      ts.load_contig(qt, Qs[buf], wave);
+      ts.load_contig(a.dout + (qt - a.q), Os[buf], wave);
     } else {
-      st.load(stid, [&](int row) -> const uint16_t* {
-        const int i = i0 + row;
-        return i < s.G ? src + orig_pos(base, i, s.N) * q_row : nullptr;
-      });
+      auto rows = [&](const uint16_t* head0) {
+        return [=, &s](int row) {
+          const int i = min(i0 + row, s.G - 1);
+          return head0 + orig_pos(base, i, s.N) * q_row;
+        };
+      };
+      ts.load_rows(rows(a.q + head_off), Qs[buf], wave, lane);
+      ts.load_rows(rows(a.dout + head_off), Os[buf], wave, lane);
     }
     if (tid < 2 * kBMQ) {
       const int i = i0 + (tid & (kBMQ - 1));
@@ -327,113 +313,152 @@ __global__ __launch_bounds__(kDkdvWaves * 64) void dkdv_kernel(BwdArgs a, RopeTa
         stat = i < s.G ? a.delta[so + orig_pos(base, i, s.N)] : 0.f;
     }
   };
-  auto store_step = [&](int buf) {
-    if (stage_dout)
-      st.store(stid, Os[buf], Ot[buf]);
-    else
-      st.store(stid, Qs[buf], Qt[buf]);
+  auto store_step = [&](int step) {
+    const int buf = step % kStages;
     if (tid < kBMQ)
       Lse2[buf][tid] = stat;
     else if (tid < 2 * kBMQ)
       Dlt[buf][tid - kBMQ] = stat;
   };
 
-  auto compute = [&](int step, auto mask_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    const int cur = step & 1;
+  // Row offset of a step inside its q head's block sequence, and whether a
+  // step's rows can see any of this pair's keys / cross its diagonal.
+  auto step_i0 = [&](int step) {
     const int hi = step / steps_per_head;
-    const int i0 = key_start + (step - hi * steps_per_head) * kBMQ;
-    // S = Q K^T and dP = dO V^T: lane column = this lane's key, elements run
-    // over the step's rows 8*(r/4) + 4*hh + r%4.  Two independent chains,
-    // fragments read one k-step ahead.
-    f32x16 sc = zero16(), dp = zero16();
+    return key_start + (step - hi * steps_per_head) * kBMQ;
+  };
+
+  // P wave: S = Q K^T (lane column = key, elements = rows
+  // 8*(r/4) + 4*hh + r%4 of the step), P = exp2(S*c*log2e - lse*log2e),
+  // publish P, dV^T += dO^T P.
+  auto p_step = [&](int step, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const int buf = step % kStages;
+    const int i0 = step_i0(step);
+    f32x16 sc = zero16();
     {
-      const uint16_t* qp = &Qs[cur][l32 * Stage::STR + hh * 8];
-      const uint16_t* op = &Os[cur][l32 * Stage::STR + hh * 8];
-      bf16x8 qa[2], oa[2];
-      qa[0] = lds_frag(qp);
-      oa[0] = lds_frag(op);
+      bf16x8 qa[2];
+      qa[0] = sw.row(Qs[buf], 0, 0);
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
-        if (kk + 1 < D / 16) {
-          qa[(kk + 1) & 1] = lds_frag(qp + (kk + 1) * 16);
-          oa[(kk + 1) & 1] = lds_frag(op + (kk + 1) * 16);
-        }
-        sc = mfma32x32x16(qa[kk & 1], kf[kk], sc);
-        dp = mfma32x32x16(oa[kk & 1], vf[kk], dp);
+        if (kk + 1 < D / 16) qa[(kk + 1) & 1] = sw.row(Qs[buf], 0, kk + 1);
+        sc = mfma32x32x16(qa[kk & 1], kvf[kk], sc);
       }
     }
-    float p[16], ds[16];
+    float p[16];
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const int row0 = 8 * r4 + 4 * hh;
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&Lse2[cur][row0]);
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&Dlt[cur][row0]);
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&Lse2[buf][row0]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int r = r4 * 4 + e;
-        float pv = fast_exp2(sc[r] * a.scale_log2 - l4[e]);
+        float pv = fast_exp2(sc[r4 * 4 + e] * a.scale_log2 - l4[e]);
         if constexpr (MASK) {
           if (kj > i0 + row0 + e) pv = 0.f;
         }
-        p[r] = pv;
+        p[r4 * 4 + e] = pv;
+      }
+    }
+    bf16x8 pb[2];
+    pb[0] = cvt8(f32x8{p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]});
+    pb[1] = cvt8(f32x8{p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]});
+    Pbuf[step & 1][pair][0][lane] = __builtin_bit_cast(u32x4, pb[0]);
+    Pbuf[step & 1][pair][1][lane] = __builtin_bit_cast(u32x4, pb[1]);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      bf16x8 ofr[D / 32];
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) ofr[db] = sw.tr(Os[buf], hf * 16, db);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) acc[db] = mfma32x32x16(ofr[db], pb[hf], acc[db]);
+    }
+  };
+
+  // dS wave (one step behind): dP = dO V^T, dS = P (dP - Delta) with the P
+  // wave's published P, dK^T += Q^T dS.
+  auto ds_step = [&](int step) {
+    const int buf = step % kStages;
+    f32x16 dp = zero16();
+    {
+      bf16x8 oa[2];
+      oa[0] = sw.row(Os[buf], 0, 0);
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        if (kk + 1 < D / 16) oa[(kk + 1) & 1] = sw.row(Os[buf], 0, kk + 1);
+        dp = mfma32x32x16(oa[kk & 1], kvf[kk], dp);
+      }
+    }
+    const bf16x8 pb0 = __builtin_bit_cast(bf16x8, Pbuf[step & 1][pair][0][lane]);
+    const bf16x8 pb1 = __builtin_bit_cast(bf16x8, Pbuf[step & 1][pair][1][lane]);
+    float ds[16];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int row0 = 8 * r4 + 4 * hh;
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&Dlt[buf][row0]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = r4 * 4 + e;
+        const float pv = (float)(r < 8 ? pb0[r] : pb1[r - 8]);
         ds[r] = pv * (dp[r] - d4[e]);
       }
     }
-    bf16x8 pb[2], dsb[2];
-    pb[0] = cvt8(f32x8{p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]});
-    pb[1] = cvt8(f32x8{p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]});
+    bf16x8 dsb[2];
     dsb[0] = cvt8(f32x8{ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]});
     dsb[1] = cvt8(f32x8{ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]});
-    // dV^T += dO^T P and dK^T += Q^T dS: 2*D/32 independent accumulators.
-    {
-      const uint16_t* otp = &Ot[cur][l32 * Stage::TSTR + hh * 8];
-      const uint16_t* qtp = &Qt[cur][l32 * Stage::TSTR + hh * 8];
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        bf16x8 ofr[D / 32], qfr[D / 32];
+    for (int hf = 0; hf < 2; ++hf) {
+      bf16x8 qfr[D / 32];
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          ofr[db] = lds_frag(otp + db * 32 * Stage::TSTR + hf * 16);
-          qfr[db] = lds_frag(qtp + db * 32 * Stage::TSTR + hf * 16);
-        }
+      for (int db = 0; db < D / 32; ++db) qfr[db] = sw.tr(Qs[buf], hf * 16, db);
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          dv[db] = mfma32x32x16(ofr[db], pb[hf], dv[db]);
-          dk[db] = mfma32x32x16(qfr[db], dsb[hf], dk[db]);
-        }
-      }
+      for (int db = 0; db < D / 32; ++db) acc[db] = mfma32x32x16(qfr[db], dsb[hf], acc[db]);
     }
   };
 
-  auto do_step = [&](int step, bool active, auto mask_tag) {
-    if (step + 1 < nsteps) load_step(step + 1);
-    if (active) compute(step, mask_tag);
-    if (step + 1 < nsteps) store_step((step & 1) ^ 1);
-    __syncthreads();
+  // Per q head: steps whose rows all precede this pair's keys contribute
+  // nothing and are skipped, the step crossing the diagonal is masked.
+  const int skip = min(steps_per_head, (kw0 - key_start) / kBMQ);
+  const int diag_end = min(steps_per_head, (kw0 + 31 - key_start) / kBMQ + 1);
+  auto step_kind = [&](int step) {  // 0 skip, 1 masked, 2 full
+    const int j = step % steps_per_head;
+    return j < skip ? 0 : (j < diag_end ? 1 : 2);
   };
 
+  // Prologue: stage step 0.
   if (nsteps > 0) {
     load_step(0);
     store_step(0);
   }
+  wait_vmem_all();
   __syncthreads();
 
-  // Per q head: steps whose rows all precede this wave's keys are skipped,
-  // steps crossing the diagonal are masked, the rest run unmasked.  The step
-  // sequence (and so the barrier count) is the same for every wave.
-  const int skip = min(steps_per_head, (kw0 - key_start) / kBMQ);   // rows < kw0 only
-  const int diag_end = min(steps_per_head, (kw0 + 31 - key_start) / kBMQ + 1);
-  for (int hi = 0; hi < rq; ++hi) {
-    const int s0 = hi * steps_per_head;
-    for (int j = 0; j < skip; ++j) do_step(s0 + j, false, std::false_type{});
-    for (int j = skip; j < diag_end; ++j) do_step(s0 + j, true, std::true_type{});
-    for (int j = diag_end; j < steps_per_head; ++j) do_step(s0 + j, true, std::false_type{});
+  // Iteration n: the P wave does step n (buffer n%3), the dS wave step n-1
+  // (buffer (n-1)%3), and everyone stages step n+1 into buffer (n+1)%3,
+  // which neither role reads during iteration n.  nsteps+1 iterations in
+  // all, identical for every wave.
+  for (int n = 0; n <= nsteps; ++n) {
+    if (n + 1 < nsteps) load_step(n + 1);
+    if (!ds_wave) {
+      if (n < nsteps) {
+        const int kind = step_kind(n);
+        if (kind == 2)
+          p_step(n, std::false_type{});
+        else if (kind == 1)
+          p_step(n, std::true_type{});
+      }
+    } else {
+      if (n >= 1 && step_kind(n - 1) != 0) ds_step(n - 1);
+    }
+    if (n + 1 < nsteps) store_step(n + 1);
+    wait_vmem_all();
+    __syncthreads();
   }
 
   if (kvalid) {
-    store_row_acc<D, ROPE>(a.dk + koff, dk, a.scale, hh, kpos, rope);
-    store_row_acc<D, false>(a.dv + koff, dv, 1.f, hh, kpos, rope);
+    if (ds_wave)
+      store_row_acc<D, ROPE>(a.dk + koff, acc, a.scale, hh, kpos, rope);
+    else
+      store_row_acc<D, false>(a.dv + koff, acc, 1.f, hh, kpos, rope);
   }
 }
 

@@ -7,7 +7,8 @@
 //   C (32 x 32):  lane l -> col l%32, element r = 0..15 -> row 8*(r/4) + 4*(l/32) + r%4
 // A product whose reduction index is permuted identically in A and B is
 // unchanged, which the kernels use to feed a C tile straight back in as a
-// B operand without moving data between lanes.
+// B operand without moving data between lanes (the matching A operand is
+// read with ds_read_b64_tr_b16 in that permuted row order).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -57,10 +58,6 @@ __device__ __forceinline__ u32x2 cvt4_bits(float a, float b, float c, float d) {
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Pack the low (or high) bf16 halves of two words into one word: (a, b).
-__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
-__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
-
 // Reductions across the two wave halves (lanes l and l^32), which hold the
 // two halves of one row of a C tile.  v_permlane32_swap exchanges the upper
 // half of its first operand with the lower half of its second; with both
@@ -93,15 +90,6 @@ __device__ __forceinline__ int xcd_logical_id(int id, int total) {
 __device__ __forceinline__ int orig_pos(int base, int j, int N) {
   const int p = base + j;
   return p >= N ? p - N : p;
-}
-
-// Position of key j (0..15) inside a 16-key block of a transposed LDS tile.
-// A lane with lane/32 = hh reads the 8 consecutive slots 8*hh..8*hh+7; these
-// must hold keys {8*(s/4) + 4*hh + s%4}, the rows a C tile gives that lane.
-// Quads 0,2 go to slots 0..7 and quads 1,3 to slots 8..15.
-__device__ __forceinline__ int tr_slot(int j16) {
-  const int q = j16 >> 2;
-  return (((q & 1) << 3) | ((q & 2) << 1)) + (j16 & 3);
 }
 
 // RoPE: rotate the 4 pairs held in 8 consecutive bf16 (d0 .. d0+7, d0 even)

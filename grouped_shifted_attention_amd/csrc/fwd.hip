@@ -8,13 +8,14 @@
 // definition); the output row is written back to the same original position,
 // which is the roll back by +shift_h.
 //
-// Per k/v tile of BN = 64 keys, staged in LDS (double-buffered, the next
-// tile's global loads in flight during the current tile's math):
+// Per k/v tile of BN = 64 keys, loaded straight into LDS (double-buffered;
+// the next tile's loads are in flight during the current tile's math):
 //   S^T = K Q^T           MFMA, A = K rows from LDS, B = Q held in VGPRs
 //   causal mask           only on tiles that cross the wave's diagonal
 //   online softmax        exp2 domain; row max/sum need one lane swap (l^32)
-//   O^T += V^T P^T        MFMA, A = V^T from a transposed LDS tile,
-//                         B = P taken straight from the S^T accumulators
+//   O^T += V^T P^T        MFMA, A = V^T read transposed (ds_read_b64_tr_b16)
+//                         from the row-major V tile, B = P taken straight
+//                         from the S^T accumulators
 // Computing S^T (not S) leaves each lane with one query row, so the softmax
 // statistics and the rescale of O are per-lane scalars.
 #include "device_common.hpp"
@@ -32,17 +33,16 @@ constexpr float kLazy = 8.f;  // log2-domain slack before the softmax reference 
 
 template <int D, int NW, bool ROPE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_kernel(FwdArgs a, RopeTable rope) {
-  constexpr int NT = NW * 64;
   constexpr int BM = NW * 32;
-  using KStage = RowStage<D, kBN, NT>;
-  using VStage = QuadStage<D, kBN, NT>;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kBN * KStage::STR];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VStage::TSTR];
+  using TileStage = LdsStage<D, kBN, NW>;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kBN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kBN * D];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep it scalar
   const int lane = tid & 63;
   const int l32 = lane & 31, hh = lane >> 5;
+  const SwzLane<D> sw(lane);
   const Shape& s = a.s;
 
   // Work item: heavy (long causal rows) tiles first within a unit; units
@@ -89,28 +89,27 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int rows_end = min((t + 1) * BM, s.G);
   const int ntiles = (rows_end + kBN - 1) / kBN;
 
-  KStage kst;
-  VStage vst;
+  const TileStage ts(wave, lane, (int)kv_row);
+  // K and V tiles go straight from global memory into the swizzled LDS
+  // tiles; rows past the group end point at the group's last row (their
+  // keys are masked, so the values never contribute).
   auto load_tile = [&](int n) {
     const int key0 = n * kBN;
+    const int buf = n & 1;
     const uint16_t* kt = contig_tile(kb_ptr, kv_row, base, key0, kBN, s.G, s.N);
     if (kt != nullptr) {
-      kst.load_contig(tid, kt, (int)kv_row);
-      vst.load_contig(tid, vb_ptr + (kt - kb_ptr), (int)kv_row);
+      ts.load_contig(kt, Ks[buf], wave);
+      ts.load_contig(vb_ptr + (kt - kb_ptr), Vs[buf], wave);
     } else {
-      kst.load(tid, [&](int row) -> const uint16_t* {
-        const int j = key0 + row;
-        return j < s.G ? kb_ptr + orig_pos(base, j, s.N) * kv_row : nullptr;
-      });
-      vst.load(tid, [&](int row) -> const uint16_t* {
-        const int j = key0 + row;
-        return j < s.G ? vb_ptr + orig_pos(base, j, s.N) * kv_row : nullptr;
-      });
+      auto rows = [&](const uint16_t* head0) {
+        return [=, &s](int row) {
+          const int j = min(key0 + row, s.G - 1);
+          return head0 + orig_pos(base, j, s.N) * kv_row;
+        };
+      };
+      ts.load_rows(rows(kb_ptr), Ks[buf], wave, lane);
+      ts.load_rows(rows(vb_ptr), Vs[buf], wave, lane);
     }
-  };
-  auto store_tile = [&](int buf) {
-    kst.store(tid, Ks[buf]);
-    vst.store(tid, nullptr, Vt[buf]);
   };
 
   // One k/v tile: S^T = K Q^T, online softmax, O^T += V^T P^T.  MASK is set
@@ -126,16 +125,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
     for (int kb = 0; kb < kBN / 32; ++kb) sc[kb] = zero16();
     {
-      const uint16_t* kp = &Ks[cur][l32 * KStage::STR + hh * 8];
+      const uint16_t* kt = Ks[cur];
       bf16x8 kf[2][kBN / 32];
 #pragma unroll
-      for (int kb = 0; kb < kBN / 32; ++kb) kf[0][kb] = lds_frag(kp + kb * 32 * KStage::STR);
+      for (int kb = 0; kb < kBN / 32; ++kb) kf[0][kb] = sw.row(kt, kb * 32, 0);
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
         if (kk + 1 < D / 16) {
 #pragma unroll
           for (int kb = 0; kb < kBN / 32; ++kb)
-            kf[(kk + 1) & 1][kb] = lds_frag(kp + kb * 32 * KStage::STR + (kk + 1) * 16);
+            kf[(kk + 1) & 1][kb] = sw.row(kt, kb * 32, kk + 1);
         }
 #pragma unroll
         for (int kb = 0; kb < kBN / 32; ++kb) sc[kb] = mfma32x32x16(kf[kk & 1][kb], qf[kk], sc[kb]);
@@ -189,19 +188,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
                              sc[kb][12], sc[kb][13], sc[kb][14], sc[kb][15]});
     }
     // O^T += V^T P^T: the D/32 output blocks are independent accumulators,
-    // cycled in the inner loop; V^T fragments are read one step ahead.
+    // cycled in the inner loop; V^T fragments come from the row-major V tile
+    // through the transposing read, one step ahead.
     {
-      const uint16_t* vp = &Vt[cur][l32 * VStage::TSTR + hh * 8];
+      const uint16_t* vt = Vs[cur];
       constexpr int KS = kBN / 16;  // 16-key reduction steps per tile
       bf16x8 vf[2][D / 32];
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) vf[0][db] = lds_frag(vp + db * 32 * VStage::TSTR);
+      for (int db = 0; db < D / 32; ++db) vf[0][db] = sw.tr(vt, 0, db);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         if (ks + 1 < KS) {
 #pragma unroll
-          for (int db = 0; db < D / 32; ++db)
-            vf[(ks + 1) & 1][db] = lds_frag(vp + db * 32 * VStage::TSTR + (ks + 1) * 16);
+          for (int db = 0; db < D / 32; ++db) vf[(ks + 1) & 1][db] = sw.tr(vt, (ks + 1) * 16, db);
         }
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
@@ -213,12 +212,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   auto step = [&](int n, auto mask_tag) {
     if (n + 1 < ntiles) load_tile(n + 1);
     compute(n, mask_tag);
-    if (n + 1 < ntiles) store_tile((n & 1) ^ 1);
+    wait_vmem_all();
     __syncthreads();
   };
 
   load_tile(0);
-  store_tile(0);
+  wait_vmem_all();
   __syncthreads();
 
   // Tiles whose keys all precede this wave's first row need no mask; the

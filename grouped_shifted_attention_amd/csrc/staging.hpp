@@ -1,153 +1,89 @@
-// Global -> VGPR -> LDS staging of bf16 row tiles for the S2-Attn kernels.
+// Global -> LDS staging of bf16 row tiles for the S2-Attn kernels, and the
+// LDS read helpers that turn them into MFMA operands.
 //
 // A tile is R rows x D columns of a [rows, heads, D] tensor whose rows are
-// gathered through the roll/group index map (the caller's `addr(row)`
-// returns the row's global address, or nullptr for rows past the group end,
-// which are staged as zeros).  Loads are issued one tile ahead (into VGPRs)
-// and written to LDS after the current tile's math, so global latency hides
-// behind MFMA work.
+// gathered through the roll/group index map.  Tiles are loaded one step
+// ahead, straight into LDS, so global latency hides behind MFMA work.
 //
-// Two LDS layouts:
-//   row-major   [R][D + 8]     rows are MFMA A operands with k = d
-//                              (16-byte reads; the 16-byte pad spreads the
-//                              rows of one read over the banks)
-//   transposed  [D][R + 8]     rows are MFMA A operands with k = tile row;
-//                              inside every 16-row block the rows sit in the
-//                              order tr_slot() gives, which matches the rows
-//                              a C accumulator hands each lane (see
-//                              device_common.hpp), so one 16-byte read per
-//                              lane fetches a whole k-slice.
+// LDS layout: row-major [R][D] with the 16-byte chunks of each row XOR-
+// swizzled: logical chunk c of row r is stored at chunk c ^ swz(r),
+// swz(r) = 2*(r & 3) + ((r >> 2) & 1).  A row is an MFMA operand with k = d
+// (one 16-byte read per lane, 8 consecutive rows per read pass); a column
+// block is an MFMA operand with k = row through the transposing LDS read
+// (4 consecutive rows x 32 bytes per 16 lanes).  The swizzle puts both read
+// shapes, and the row writes, on distinct banks; no single row padding can.
 #pragma once
 
 #include "device_common.hpp"
 
 namespace s2a {
 
-// Row-major copy.  Items are 16-byte chunks, chunk index fastest, so a wave's
-// global loads are contiguous row segments and its LDS writes hit distinct
-// banks.
-template <int D, int R, int NT>
-struct RowStage {
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
+// Direct global -> LDS staging (global_load_lds_dwordx4) of an R x D tile
+// into the swizzled layout; no VGPRs hold the data.  One wave instruction
+// moves 64 lanes x 16 bytes into 1 KB of LDS, lane l's bytes at +16*l, so
+// instruction `inst` fills tile chunks 64*inst .. 64*inst+63, i.e. physical
+// chunk p = q % (D/8) of row q / (D/8); the lane fetches the logical chunk
+// p ^ swz(row) from global memory.  The NW waves of the workgroup split the
+// R*D/512 instructions round-robin.  Completion is tracked by vmcnt: wait
+// (s_waitcnt vmcnt) and barrier before the tile is read.
+template <int D, int R, int NW>
+struct LdsStage {
   static constexpr int CH = D / 8;
-  static constexpr int ITEMS = R * CH;
-  static constexpr int PER = (ITEMS + NT - 1) / NT;
-  static constexpr int STR = D + 8;
-  u32x4 r[PER];
+  static constexpr int INSTR = R * CH / 64;
+  static constexpr int PER = (INSTR + NW - 1) / NW;
+  static_assert(R * CH % 64 == 0, "tile must be a whole number of 1 KB wave loads");
+  int off[PER];  // fast path: element offset of the lane's chunk in a contiguous tile
 
-  template <class Addr>
-  __device__ __forceinline__ void load(int tid, Addr addr) {
+  __device__ __forceinline__ static int chunk_row(int inst, int lane) { return (inst * 64 + lane) / CH; }
+  __device__ __forceinline__ static int chunk_col(int inst, int lane) {
+    const int q = inst * 64 + lane;
+    return ((q % CH) ^ swz(q / CH)) << 3;
+  }
+
+  __device__ __forceinline__ LdsStage(int wave, int lane, int row_stride) {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int item = tid + i * NT;
-      if (ITEMS % NT == 0 || item < ITEMS) {
-        const int row = item / CH, ch = item % CH;
-        const uint16_t* p = addr(row);
-        r[i] = p ? ld16(p + ch * 8) : zero_u4();
-      }
+    for (int k = 0; k < PER; ++k) {
+      const int inst = wave + k * NW;
+      off[k] = chunk_row(inst, lane) * row_stride + chunk_col(inst, lane);
     }
   }
 
-  // Fast path: the R rows are consecutive rows of the tensor starting at
-  // `tile0` (no group end, no wrap inside the tile), `row_stride` elements
-  // apart.  The per-thread offset is loop-invariant, so each load is one
-  // instruction off a uniform base.
-  __device__ __forceinline__ void load_contig(int tid, const uint16_t* tile0, int row_stride) {
+  __device__ __forceinline__ static void dma(const uint16_t* src, uint16_t* dst) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+  }
+
+  // R consecutive rows starting at `tile0` (see contig_tile).
+  __device__ __forceinline__ void load_contig(const uint16_t* tile0, uint16_t* lds, int wave) const {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int item = tid + i * NT;
-      if (ITEMS % NT == 0 || item < ITEMS) {
-        const int row = item / CH, ch = item % CH;
-        r[i] = ld16(tile0 + (row * row_stride + ch * 8));
-      }
+    for (int k = 0; k < PER; ++k) {
+      const int inst = wave + k * NW;
+      if (INSTR % NW == 0 || inst < INSTR) dma(tile0 + off[k], lds + inst * 512);
     }
   }
 
-  __device__ __forceinline__ void store(int tid, uint16_t* lds) const {
+  // General rows: `row_ptr(r)` must return a readable row for every r < R
+  // (callers point rows past the group end at a valid row; those rows only
+  // ever meet exact-zero weights).
+  template <class RowPtr>
+  __device__ __forceinline__ void load_rows(RowPtr row_ptr, uint16_t* lds, int wave, int lane) const {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int item = tid + i * NT;
-      if (ITEMS % NT == 0 || item < ITEMS) {
-        const int row = item / CH, ch = item % CH;
-        *reinterpret_cast<u32x4*>(lds + row * STR + ch * 8) = r[i];
-      }
+    for (int k = 0; k < PER; ++k) {
+      const int inst = wave + k * NW;
+      if (INSTR % NW == 0 || inst < INSTR)
+        dma(row_ptr(chunk_row(inst, lane)) + chunk_col(inst, lane), lds + inst * 512);
     }
   }
 };
 
-// Quad copy: items are (4-row quad, 8-column octet) blocks, quad index
-// fastest.  Feeds the transposed layout (each thread owns 4 rows x 8 columns
-// and writes 8 columns x 4 rows as 8-byte words, the quads of one wave
-// landing in distinct banks) and optionally the row-major layout too.
-template <int D, int R, int NT>
-struct QuadStage {
-  static constexpr int CH = D / 8;
-  static constexpr int NQ = R / 4;
-  static constexpr int ITEMS = NQ * CH;
-  static constexpr int PER = (ITEMS + NT - 1) / NT;
-  static constexpr int STR = D + 8;
-  static constexpr int TSTR = R + 8;
-  u32x4 r[PER][4];
-
-  template <class Addr>
-  __device__ __forceinline__ void load(int tid, Addr addr) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int item = tid + i * NT;
-      if (ITEMS % NT == 0 || item < ITEMS) {
-        const int rq = item % NQ, oc = item / NQ;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const uint16_t* p = addr(rq * 4 + u);
-          r[i][u] = p ? ld16(p + oc * 8) : zero_u4();
-        }
-      }
-    }
-  }
-
-  // Fast path for R consecutive rows starting at `tile0` (see RowStage).
-  __device__ __forceinline__ void load_contig(int tid, const uint16_t* tile0, int row_stride) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int item = tid + i * NT;
-      if (ITEMS % NT == 0 || item < ITEMS) {
-        const int rq = item % NQ, oc = item / NQ;
-        const int off = rq * 4 * row_stride + oc * 8;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) r[i][u] = ld16(tile0 + u * row_stride + off);
-      }
-    }
-  }
-
-  // row_lds may be nullptr (transposed copy only).
-  __device__ __forceinline__ void store(int tid, uint16_t* row_lds, uint16_t* tr_lds) const {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int item = tid + i * NT;
-      if (ITEMS % NT == 0 || item < ITEMS) {
-        const int rq = item % NQ, oc = item / NQ;
-        if (row_lds != nullptr) {
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            *reinterpret_cast<u32x4*>(row_lds + (rq * 4 + u) * STR + oc * 8) = r[i][u];
-        }
-        const int pos = (rq >> 2) * 16 + tr_slot((rq & 3) * 4);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int w = e >> 1;
-          u32x2 pr;
-          if (e & 1) {
-            pr[0] = pack_hi(r[i][0][w], r[i][1][w]);
-            pr[1] = pack_hi(r[i][2][w], r[i][3][w]);
-          } else {
-            pr[0] = pack_lo(r[i][0][w], r[i][1][w]);
-            pr[1] = pack_lo(r[i][2][w], r[i][3][w]);
-          }
-          *reinterpret_cast<u32x2*>(tr_lds + (oc * 8 + e) * TSTR + pos) = pr;
-        }
-      }
-    }
-  }
-};
+// Wait until this wave's outstanding global loads (including LDS DMA) have
+// completed; other counters are left alone.
+__device__ __forceinline__ void wait_vmem_all() {
+  // gfx9 s_waitcnt immediate: vmcnt = 0, expcnt = 7 (no wait), lgkmcnt = 15 (no wait)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
 
 // Start of a tile of R local rows beginning at local row j0 of a group whose
 // first rolled row is at original position `base`, if those R rows are R
@@ -165,5 +101,61 @@ __device__ __forceinline__ const uint16_t* contig_tile(const uint16_t* head0, lo
 __device__ __forceinline__ bf16x8 lds_frag(const uint16_t* p) {
   return as_bf16x8(*reinterpret_cast<const u32x4*>(p));
 }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i supplies 4
+// consecutive 16-bit elements M[4i..4i+3]; lane j receives M[j], M[16+j],
+// M[32+j], M[48+j].  Four lanes pointing at 4 consecutive columns of one row
+// thus form one row of a 4 x 16 block, and every lane receives one column of
+// it across the 4 rows.
+__device__ __forceinline__ s16x4 lds_read_tr(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+}
+
+// Per-lane addressing of the swizzled tiles, computed once per kernel.
+//
+// Row read (MFMA operand with k = d): the lane's row is rb + lane%32 (rb a
+// multiple of 8), k-step kk covers logical chunk 2*kk + lane/32.  Because
+// swz() only touches the low 3 chunk bits and depends only on row % 8, the
+// offset is rb*D + 64*(kk/4) + row_off[kk%4].
+//
+// Transposed read (MFMA A operand with k = tile row): lane l belongs to group
+// g = l/16 (hh = g/2 picks the row half, g%2 the 16-column half) and has
+// i = l%16 (row i/4 of a 4-row block, 4-element column chunk i%4).  Element
+// s of a lane in half hh is row k0 + 8*(s/4) + 4*hh + s%4 (the order a C
+// accumulator hands a lane its rows) and its column is 32*db + lane%32; the
+// offset is k0*D + 64*(db/2) + tr_off[db%2] (+ 8*D for the second 4 rows).
+template <int D>
+struct SwzLane {
+  int row_off[4];
+  int tr_off[2];
+
+  __device__ __forceinline__ explicit SwzLane(int lane) {
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int y = hh ^ swz(l32 & 7);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) row_off[q] = l32 * D + (((2 * q) ^ y) << 3);
+    const int g = lane >> 4, i = lane & 15;
+    const int r = 4 * (g >> 1) + (i >> 2);
+    const int lc = 2 * (g & 1) + ((i & 3) >> 1);
+#pragma unroll
+    for (int od = 0; od < 2; ++od) tr_off[od] = r * D + (((4 * od + lc) ^ swz(r)) << 3) + 4 * (i & 1);
+  }
+
+  __device__ __forceinline__ bf16x8 row(const uint16_t* tile, int rb, int kk) const {
+    return lds_frag(tile + rb * D + ((kk >> 2) << 6) + row_off[kk & 3]);
+  }
+
+  __device__ __forceinline__ bf16x8 tr(const uint16_t* tile, int k0, int db) const {
+    const uint16_t* p = tile + k0 * D + ((db >> 1) << 6) + tr_off[db & 1];
+    const s16x4 lo = lds_read_tr(p);
+    const s16x4 hi = lds_read_tr(p + 8 * D);  // swz(r + 8) == swz(r)
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+  }
+};
 
 }  // namespace s2a
