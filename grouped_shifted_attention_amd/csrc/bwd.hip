@@ -71,8 +71,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
                                                                                                  RopeTable rope) {
   constexpr int BM = NW * 32;
   using TileStage = LdsStage<D, kBN, NW>;  // K rows (S^T; read transposed for dQ^T), V rows (dP^T)
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kBN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kBN * D];
+  constexpr int NBUF = NW >= 8 ? 3 : 2;    // tiles in LDS (loads NBUF-1 ahead)
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[NBUF][kBN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[NBUF][kBN * D];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep it scalar
@@ -120,7 +121,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const TileStage ts(wave, lane, (int)kv_row);
   auto load_tile = [&](int n) {
     const int key0 = n * kBN;
-    const int buf = n & 1;
+    const int buf = n % NBUF;
     const uint16_t* kt = contig_tile(kb_ptr, kv_row, base, key0, kBN, s.G, s.N);
     if (kt != nullptr) {
       ts.load_contig(kt, Ks[buf], wave);
@@ -139,7 +140,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
   auto compute = [&](int n, auto mask_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    const int cur = n & 1;
+    const int cur = n % NBUF;
     const int key0 = n * kBN;
     // Two 32-key halves in turn (keeps the live S/dP set small enough for
     // two waves per SIMD).  Per half: S^T = K Q^T and dP^T = V dO^T (two
@@ -187,15 +188,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
   };
 
+  const int loads_per_tile = 2 * TileStage::count(wave);
   auto step = [&](int n, auto mask_tag) {
-    if (n + 1 < ntiles) load_tile(n + 1);
+    if (n + NBUF - 1 < ntiles) load_tile(n + NBUF - 1);
     compute(n, mask_tag);
-    wait_vmem_all();
+    wait_vmcnt_dyn(loads_per_tile * (min(n + NBUF - 1, ntiles - 1) - (n + 1)));
     __syncthreads();
   };
 
-  load_tile(0);
-  wait_vmem_all();
+#pragma unroll
+  for (int t = 0; t < NBUF - 1; ++t)
+    if (t < ntiles) load_tile(t);
+  wait_vmcnt_dyn(loads_per_tile * (min(NBUF - 2, ntiles - 1)));
   __syncthreads();
 
   // Unmasked tiles first, then the diagonal ones (see the forward kernel).
@@ -215,13 +219,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 // step behind on the same keys and computes dP = dO V^T, dS = P (dP - Delta)
 // and dK^T += Q^T dS.  Each keeps one of K/V and one of dK/dV, which halves
 // the registers a wave needs against one wave doing all four products.
-// q/dout tiles are triple-buffered so that step n+1 stages while the two
-// roles work on steps n and n-1; one barrier per step.
+// q/dout tiles sit in a 4-deep LDS ring: while the two roles work on steps
+// n and n-1, step n+1 is resident and step n+2 is being loaded.  One barrier
+// per step.
 constexpr int kDkdvPairs = 4;
 constexpr int kDkdvWaves = 2 * kDkdvPairs;
 constexpr int kBNK = kDkdvPairs * 32;  // keys per workgroup
 constexpr int kBMQ = 32;               // q rows per step
-constexpr int kStages = 3;
+constexpr int kStages = 4;
 
 template <int D, bool ROPE>
 __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void dkdv_kernel(
@@ -304,7 +309,13 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
       ts.load_rows(rows(a.q + head_off), Qs[buf], wave, lane);
       ts.load_rows(rows(a.dout + head_off), Os[buf], wave, lane);
     }
+  };
+  // Row statistics of a step (lse in log2 units, Delta), through VGPRs.
+  auto load_stats = [&](int step) {
     if (tid < 2 * kBMQ) {
+      const int hi = step / steps_per_head;
+      const int i0 = key_start + (step - hi * steps_per_head) * kBMQ;
+      const int h = h0 + hi;
       const int i = i0 + (tid & (kBMQ - 1));
       const long long so = ((long long)b * s.H + h) * s.N;
       if (tid < kBMQ)
@@ -313,7 +324,7 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
         stat = i < s.G ? a.delta[so + orig_pos(base, i, s.N)] : 0.f;
     }
   };
-  auto store_step = [&](int step) {
+  auto store_stats = [&](int step) {
     const int buf = step % kStages;
     if (tid < kBMQ)
       Lse2[buf][tid] = stat;
@@ -424,20 +435,25 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
     return j < skip ? 0 : (j < diag_end ? 1 : 2);
   };
 
-  // Prologue: stage step 0.
+  // Order per iteration: the statistics load for step n+1 is issued before
+  // the tile loads of step n+2, so waiting for it (to store it) and waiting
+  // for step n+1's tiles both leave step n+2's loads in flight.
+  const int loads_per_step = 2 * TileStage::count(wave);
   if (nsteps > 0) {
+    load_stats(0);
     load_step(0);
-    store_step(0);
+    if (nsteps > 1) load_step(1);
+    store_stats(0);
   }
-  wait_vmem_all();
+  wait_vmcnt_dyn(nsteps > 1 ? loads_per_step : 0);
   __syncthreads();
 
-  // Iteration n: the P wave does step n (buffer n%3), the dS wave step n-1
-  // (buffer (n-1)%3), and everyone stages step n+1 into buffer (n+1)%3,
-  // which neither role reads during iteration n.  nsteps+1 iterations in
-  // all, identical for every wave.
+  // Iteration n: the P wave does step n, the dS wave step n-1; step n+1 is
+  // resident, step n+2 loads into the buffer that held step n-2.
+  // nsteps+1 iterations in all, identical for every wave.
   for (int n = 0; n <= nsteps; ++n) {
-    if (n + 1 < nsteps) load_step(n + 1);
+    if (n + 1 < nsteps) load_stats(n + 1);
+    if (n + 2 < nsteps) load_step(n + 2);
     if (!ds_wave) {
       if (n < nsteps) {
         const int kind = step_kind(n);
@@ -449,8 +465,8 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
     } else {
       if (n >= 1 && step_kind(n - 1) != 0) ds_step(n - 1);
     }
-    if (n + 1 < nsteps) store_step(n + 1);
-    wait_vmem_all();
+    if (n + 1 < nsteps) store_stats(n + 1);
+    wait_vmcnt_dyn(n + 2 < nsteps ? loads_per_step : 0);
     __syncthreads();
   }
 
@@ -489,10 +505,20 @@ hipError_t launch_dkdv_t(BwdArgs a, const RopeTable* rope, hipStream_t stream) {
 
 }  // namespace
 
+#ifndef S2A_DQ_WAVES_LARGE
+#define S2A_DQ_WAVES_LARGE 4  // waves per workgroup for groups longer than 1024
+#endif
+
+template <int D, bool ROPE>
+hipError_t launch_dq_d(const BwdArgs& a, const RopeTable* rope, hipStream_t stream) {
+  if (a.s.G <= 1024) return launch_dq_t<D, 4, ROPE>(a, rope, stream);
+  return launch_dq_t<D, S2A_DQ_WAVES_LARGE, ROPE>(a, rope, stream);
+}
+
 hipError_t launch_bwd_dq(const BwdArgs& a, const RopeTable* rope, hipStream_t stream) {
   const bool r = rope != nullptr;
-  if (a.s.D == 64) return r ? launch_dq_t<64, 4, true>(a, rope, stream) : launch_dq_t<64, 4, false>(a, rope, stream);
-  return r ? launch_dq_t<128, 4, true>(a, rope, stream) : launch_dq_t<128, 4, false>(a, rope, stream);
+  if (a.s.D == 64) return r ? launch_dq_d<64, true>(a, rope, stream) : launch_dq_d<64, false>(a, rope, stream);
+  return r ? launch_dq_d<128, true>(a, rope, stream) : launch_dq_d<128, false>(a, rope, stream);
 }
 
 hipError_t launch_bwd_dkdv(const BwdArgs& a, const RopeTable* rope, hipStream_t stream) {

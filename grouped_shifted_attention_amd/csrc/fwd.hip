@@ -31,12 +31,22 @@ namespace {
 constexpr int kBN = 64;
 constexpr float kLazy = 8.f;  // log2-domain slack before the softmax reference moves
 
-template <int D, int NW, bool ROPE>
+// VCOPY: V reaches LDS as a transposed copy through VGPRs (plain 16-byte
+// reads for O^T += V^T P^T); otherwise V is loaded straight into LDS and read
+// with the transposing LDS read.
+template <int D, int NW, bool ROPE, bool VCOPY>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_kernel(FwdArgs a, RopeTable rope) {
   constexpr int BM = NW * 32;
   using TileStage = LdsStage<D, kBN, NW>;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kBN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kBN * D];
+  using VtStage = TransposeStage<D, kBN, NW * 64>;
+  // Eight-wave workgroups (one per CU) keep three tiles in LDS and load two
+  // ahead; smaller ones (two per CU) keep two and load one ahead.  The VGPR
+  // transposed copy of V is always one tile ahead.
+  constexpr int NBUF = (NW >= 8 && !VCOPY) ? 3 : 2;
+  constexpr int VELEMS = VCOPY ? D * VtStage::TSTR : kBN * D;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[NBUF][kBN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[NBUF][VELEMS];
+  VtStage vts;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep it scalar
@@ -95,20 +105,26 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // keys are masked, so the values never contribute).
   auto load_tile = [&](int n) {
     const int key0 = n * kBN;
-    const int buf = n & 1;
+    const int buf = n % NBUF;
     const uint16_t* kt = contig_tile(kb_ptr, kv_row, base, key0, kBN, s.G, s.N);
+    auto rows = [&](const uint16_t* head0) {
+      return [=, &s](int row) {
+        const int j = min(key0 + row, s.G - 1);
+        return head0 + orig_pos(base, j, s.N) * kv_row;
+      };
+    };
     if (kt != nullptr) {
       ts.load_contig(kt, Ks[buf], wave);
-      ts.load_contig(vb_ptr + (kt - kb_ptr), Vs[buf], wave);
+      if constexpr (VCOPY)
+        vts.load_contig(tid, vb_ptr + (kt - kb_ptr), (int)kv_row);
+      else
+        ts.load_contig(vb_ptr + (kt - kb_ptr), Vs[buf], wave);
     } else {
-      auto rows = [&](const uint16_t* head0) {
-        return [=, &s](int row) {
-          const int j = min(key0 + row, s.G - 1);
-          return head0 + orig_pos(base, j, s.N) * kv_row;
-        };
-      };
       ts.load_rows(rows(kb_ptr), Ks[buf], wave, lane);
-      ts.load_rows(rows(vb_ptr), Vs[buf], wave, lane);
+      if constexpr (VCOPY)
+        vts.load_rows(tid, rows(vb_ptr));
+      else
+        ts.load_rows(rows(vb_ptr), Vs[buf], wave, lane);
     }
   };
 
@@ -116,7 +132,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // only for tiles that reach past this wave's first row (the diagonal).
   auto compute = [&](int n, auto mask_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    const int cur = n & 1;
+    const int cur = n % NBUF;
     const int key0 = n * kBN;
     // S^T: the two 32-key blocks are independent accumulators, interleaved
     // so back-to-back MFMAs never wait on each other; K fragments are read
@@ -193,14 +209,20 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     {
       const uint16_t* vt = Vs[cur];
       constexpr int KS = kBN / 16;  // 16-key reduction steps per tile
+      auto vfrag = [&](int ks, int db) -> bf16x8 {
+        if constexpr (VCOPY)
+          return lds_frag(vt + (db * 32 + l32) * VtStage::TSTR + ks * 16 + hh * 8);
+        else
+          return sw.tr(vt, ks * 16, db);
+      };
       bf16x8 vf[2][D / 32];
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) vf[0][db] = sw.tr(vt, 0, db);
+      for (int db = 0; db < D / 32; ++db) vf[0][db] = vfrag(0, db);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         if (ks + 1 < KS) {
 #pragma unroll
-          for (int db = 0; db < D / 32; ++db) vf[(ks + 1) & 1][db] = sw.tr(vt, (ks + 1) * 16, db);
+          for (int db = 0; db < D / 32; ++db) vf[(ks + 1) & 1][db] = vfrag(ks + 1, db);
         }
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
@@ -209,15 +231,30 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
   };
 
+  // Tile n+1 must have landed before the barrier that ends step n; the
+  // loads of later tiles may stay in flight.
+  const int loads_per_tile = (VCOPY ? 1 : 2) * TileStage::count(wave);
   auto step = [&](int n, auto mask_tag) {
-    if (n + 1 < ntiles) load_tile(n + 1);
+    if (n + NBUF - 1 < ntiles) load_tile(n + NBUF - 1);
     compute(n, mask_tag);
-    wait_vmem_all();
+    if constexpr (VCOPY) {
+      if (n + 1 < ntiles) vts.store(tid, Vs[(n + 1) % NBUF]);
+      wait_vmem_all();
+    } else {
+      wait_vmcnt_dyn(loads_per_tile * (min(n + NBUF - 1, ntiles - 1) - (n + 1)));
+    }
     __syncthreads();
   };
 
-  load_tile(0);
-  wait_vmem_all();
+#pragma unroll
+  for (int t = 0; t < NBUF - 1; ++t)
+    if (t < ntiles) load_tile(t);
+  if constexpr (VCOPY) {
+    vts.store(tid, Vs[0]);
+    wait_vmem_all();
+  } else {
+    wait_vmcnt_dyn(loads_per_tile * (min(NBUF - 2, ntiles - 1)));
+  }
   __syncthreads();
 
   // Tiles whose keys all precede this wave's first row need no mask; the
@@ -246,6 +283,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   }
 }
 
+#ifndef S2A_FWD_WAVES_LARGE
+#define S2A_FWD_WAVES_LARGE 4  // waves per workgroup for groups longer than 1024
+#endif
+#ifndef S2A_FWD_VCOPY
+#define S2A_FWD_VCOPY 0  // V through a VGPR transposed copy (1) or transposing reads (0)
+#endif
+
 template <int D, int NW, bool ROPE>
 hipError_t launch_fwd_t(FwdArgs a, const RopeTable* rope, hipStream_t stream) {
   constexpr int BM = NW * 32;
@@ -255,15 +299,16 @@ hipError_t launch_fwd_t(FwdArgs a, const RopeTable* rope, hipStream_t stream) {
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   RopeTable rt{};
   if (ROPE) rt = *rope;
-  hipLaunchKernelGGL((fwd_kernel<D, NW, ROPE>), dim3((unsigned)grid), dim3(NW * 64), 0, stream, a, rt);
+  hipLaunchKernelGGL((fwd_kernel<D, NW, ROPE, S2A_FWD_VCOPY != 0>), dim3((unsigned)grid), dim3(NW * 64), 0, stream,
+                     a, rt);
   return hipGetLastError();
 }
 
 template <int D, bool ROPE>
 hipError_t launch_fwd_d(const FwdArgs& a, const RopeTable* rope, hipStream_t stream) {
   if (a.s.G <= 64) return launch_fwd_t<D, 2, ROPE>(a, rope, stream);
-  if (a.s.G <= 128) return launch_fwd_t<D, 4, ROPE>(a, rope, stream);
-  return launch_fwd_t<D, 4, ROPE>(a, rope, stream);
+  if (a.s.G <= 1024) return launch_fwd_t<D, 4, ROPE>(a, rope, stream);
+  return launch_fwd_t<D, S2A_FWD_WAVES_LARGE, ROPE>(a, rope, stream);
 }
 
 }  // namespace

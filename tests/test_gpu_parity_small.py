@@ -30,6 +30,9 @@ CASES = [
     ("gqa8_rope", 1, 512, 16, 2, 128, 256, 128, (10000.0, 8.0)),
     ("rope_d64_b2", 2, 256, 4, 4, 64, 128, 64, (500.0, 2.0)),
     ("ragged_rope_g160", 1, 320, 4, 2, 128, 160, 80, (10000.0, 4.0)),
+    ("g2048_large_tiles", 1, 4096, 2, 2, 128, 2048, 1024, None),
+    ("ragged_g1100_large_tiles", 1, 2200, 2, 2, 64, 1100, 550, None),
+    ("gqa_rope_g1536", 1, 3072, 4, 2, 128, 1536, 768, (10000.0, 8.0)),
 ]
 IDS = [c[0] for c in CASES]
 
