@@ -71,9 +71,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
                                                                                                  RopeTable rope) {
   constexpr int BM = NW * 32;
   using TileStage = LdsStage<D, kBN, NW>;  // K rows (S^T; read transposed for dQ^T), V rows (dP^T)
-  constexpr int NBUF = NW >= 8 ? 3 : 2;    // tiles in LDS (loads NBUF-1 ahead)
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[NBUF][kBN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[NBUF][kBN * D];
+  // Double-buffered K/V tiles as distinct LDS objects named at compile time
+  // (tile n in buffer n & 1), so reads of one buffer never wait for the
+  // direct loads into the other.
+  __shared__ __attribute__((aligned(16))) uint16_t Ks0[kBN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks1[kBN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs0[kBN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs1[kBN * D];
+  auto kbuf = [&](auto p) __attribute__((always_inline)) -> uint16_t* {
+    if constexpr (decltype(p)::value) return Ks1; else return Ks0;
+  };
+  auto vbuf = [&](auto p) __attribute__((always_inline)) -> uint16_t* {
+    if constexpr (decltype(p)::value) return Vs1; else return Vs0;
+  };
+  using P0 = std::false_type;
+  using P1 = std::true_type;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep it scalar
@@ -119,13 +131,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int ntiles = (rows_end + kBN - 1) / kBN;
 
   const TileStage ts(wave, lane, (int)kv_row);
-  auto load_tile = [&](int n) {
+  auto load_tile = [&](int n, auto p) __attribute__((always_inline)) {
     const int key0 = n * kBN;
-    const int buf = n % NBUF;
     const uint16_t* kt = contig_tile(kb_ptr, kv_row, base, key0, kBN, s.G, s.N);
     if (kt != nullptr) {
-      ts.load_contig(kt, Ks[buf], wave);
-      ts.load_contig(vb_ptr + (kt - kb_ptr), Vs[buf], wave);
+      ts.load_contig(kt, kbuf(p), wave);
+      ts.load_contig(vb_ptr + (kt - kb_ptr), vbuf(p), wave);
     } else {
       auto rows = [&](const uint16_t* head0) {
         return [=, &s](int row) {
@@ -133,14 +144,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
           return head0 + orig_pos(base, j, s.N) * kv_row;
         };
       };
-      ts.load_rows(rows(kb_ptr), Ks[buf], wave, lane);
-      ts.load_rows(rows(vb_ptr), Vs[buf], wave, lane);
+      ts.load_rows(rows(kb_ptr), kbuf(p), wave, lane);
+      ts.load_rows(rows(vb_ptr), vbuf(p), wave, lane);
     }
   };
 
-  auto compute = [&](int n, auto mask_tag) {
+  auto compute = [&](int n, auto mask_tag, auto p) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    const int cur = n % NBUF;
+    const uint16_t* kt = kbuf(p);
+    const uint16_t* vt = vbuf(p);
     const int key0 = n * kBN;
     // Two 32-key halves in turn (keeps the live S/dP set small enough for
     // two waves per SIMD).  Per half: S^T = K Q^T and dP^T = V dO^T (two
@@ -152,13 +164,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       f32x16 sc = zero16(), dp = zero16();
       {
         bf16x8 kf[2], vf[2];
-        kf[0] = sw.row(Ks[cur], kb * 32, 0);
-        vf[0] = sw.row(Vs[cur], kb * 32, 0);
+        kf[0] = sw.row(kt, kb * 32, 0);
+        vf[0] = sw.row(vt, kb * 32, 0);
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
           if (kk + 1 < D / 16) {
-            kf[(kk + 1) & 1] = sw.row(Ks[cur], kb * 32, kk + 1);
-            vf[(kk + 1) & 1] = sw.row(Vs[cur], kb * 32, kk + 1);
+            kf[(kk + 1) & 1] = sw.row(kt, kb * 32, kk + 1);
+            vf[(kk + 1) & 1] = sw.row(vt, kb * 32, kk + 1);
           }
           sc = mfma32x32x16(kf[kk & 1], qf[kk], sc);
           dp = mfma32x32x16(vf[kk & 1], dof[kk], dp);
@@ -181,31 +193,38 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       for (int hf = 0; hf < 2; ++hf) {
         bf16x8 tf[D / 32];
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) tf[db] = sw.tr(Ks[cur], kb * 32 + hf * 16, db);
+        for (int db = 0; db < D / 32; ++db) tf[db] = sw.tr(kt, kb * 32 + hf * 16, db);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) dq[db] = mfma32x32x16(tf[db], dsb[hf], dq[db]);
       }
     }
   };
 
-  const int loads_per_tile = 2 * TileStage::count(wave);
-  auto step = [&](int n, auto mask_tag) {
-    if (n + NBUF - 1 < ntiles) load_tile(n + NBUF - 1);
-    compute(n, mask_tag);
-    wait_vmcnt_dyn(loads_per_tile * (min(n + NBUF - 1, ntiles - 1) - (n + 1)));
-    __syncthreads();
+  // Step n: load tile n+1 into the other buffer, compute tile n, wait for
+  // tile n+1, barrier.  Unrolled by two so each step names its buffer.
+  auto step = [&](int n, auto mask_tag, auto p) __attribute__((always_inline)) {
+    if (n + 1 < ntiles) load_tile(n + 1, std::integral_constant<bool, !decltype(p)::value>{});
+    compute(n, mask_tag, p);
+    wait_vmem_all();
+    lds_barrier();
+  };
+  auto run = [&](int n, int n1, auto mask_tag) __attribute__((always_inline)) {
+    if (n < n1 && (n & 1)) step(n++, mask_tag, P1{});
+    for (; n + 1 < n1; n += 2) {
+      step(n, mask_tag, P0{});
+      step(n + 1, mask_tag, P1{});
+    }
+    if (n < n1) step(n, mask_tag, P0{});
   };
 
-#pragma unroll
-  for (int t = 0; t < NBUF - 1; ++t)
-    if (t < ntiles) load_tile(t);
-  wait_vmcnt_dyn(loads_per_tile * (min(NBUF - 2, ntiles - 1)));
-  __syncthreads();
+  load_tile(0, P0{});
+  wait_vmem_all();
+  lds_barrier();
 
   // Unmasked tiles first, then the diagonal ones (see the forward kernel).
   const int n_full = min(ntiles, (wave_q0 + 1) / kBN);
-  for (int n = 0; n < n_full; ++n) step(n, std::false_type{});
-  for (int n = n_full; n < ntiles; ++n) step(n, std::true_type{});
+  run(0, n_full, std::false_type{});
+  run(n_full, ntiles, std::true_type{});
 
   if (qvalid) store_row_acc<D, ROPE>(a.dq + qoff, dq, a.scale, hh, qpos, rope);
 }
@@ -220,8 +239,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 // and dK^T += Q^T dS.  Each keeps one of K/V and one of dK/dV, which halves
 // the registers a wave needs against one wave doing all four products.
 // q/dout tiles sit in a 4-deep LDS ring: while the two roles work on steps
-// n and n-1, step n+1 is resident and step n+2 is being loaded.  One barrier
-// per step.
+// n and n-1, step n+1 is resident and step n+2 is being loaded.  The rows'
+// lse and Delta ride along at the end of the dout tile.  One barrier per
+// step.
 constexpr int kDkdvPairs = 4;
 constexpr int kDkdvWaves = 2 * kDkdvPairs;
 constexpr int kBNK = kDkdvPairs * 32;  // keys per workgroup
@@ -232,10 +252,30 @@ template <int D, bool ROPE>
 __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void dkdv_kernel(
     BwdArgs a, RopeTable rope) {
   using TileStage = LdsStage<D, kBMQ, kDkdvWaves>;
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[kStages][kBMQ * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Os[kStages][kBMQ * D];
-  __shared__ __attribute__((aligned(16))) float Lse2[kStages][kBMQ];
-  __shared__ __attribute__((aligned(16))) float Dlt[kStages][kBMQ];
+  // The ring's q and dout tiles are eight distinct LDS objects, each named
+  // at compile time (step m in stage m & 3), so reads of one stage never
+  // wait for the direct loads into another.
+  __shared__ __attribute__((aligned(16))) uint16_t Q0[kBMQ * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Q1[kBMQ * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Q2[kBMQ * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Q3[kBMQ * D];
+  // dout tile, then the step's 32 lse values and 32 Delta values (fp32).
+  constexpr int kOElems = kBMQ * D + 2 * kBMQ * 2;
+  __shared__ __attribute__((aligned(16))) uint16_t O0[kOElems];
+  __shared__ __attribute__((aligned(16))) uint16_t O1[kOElems];
+  __shared__ __attribute__((aligned(16))) uint16_t O2[kOElems];
+  __shared__ __attribute__((aligned(16))) uint16_t O3[kOElems];
+  auto qbuf = [&](auto c) __attribute__((always_inline)) -> uint16_t* {
+    constexpr int C = decltype(c)::value;
+    if constexpr (C == 0) return Q0; else if constexpr (C == 1) return Q1;
+    else if constexpr (C == 2) return Q2; else return Q3;
+  };
+  auto obuf = [&](auto c) __attribute__((always_inline)) -> uint16_t* {
+    constexpr int C = decltype(c)::value;
+    if constexpr (C == 0) return O0; else if constexpr (C == 1) return O1;
+    else if constexpr (C == 2) return O2; else return O3;
+  };
+  static_assert(kStages == 4, "the ring is unrolled by four");
   // P hand-over: [buffer][pair][half][lane] 16 bytes (8 bf16).
   __shared__ __attribute__((aligned(16))) u32x4 Pbuf[2][kDkdvPairs][2][64];
 
@@ -286,19 +326,22 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
   const int nsteps = steps_per_head * rq;
 
   const TileStage ts(wave, lane, (int)q_row);
-  float stat = 0.f;
-  // q and dout rows of a step go straight into LDS; rows past the group end
-  // point at the group's last row (their P is exactly zero: lse = +inf).
-  auto load_step = [&](int step) {
+  auto stats = [&](auto c) __attribute__((always_inline)) -> float* {
+    return reinterpret_cast<float*>(obuf(c) + kBMQ * D);
+  };
+  // q and dout rows of a step go straight into LDS, and wave 0 loads the
+  // rows' lse (lanes 0-31) and Delta (lanes 32-63) behind the dout tile.
+  // Rows past the group end point at the group's last row; the P wave
+  // masks them.
+  auto load_step = [&](int step, auto c) __attribute__((always_inline)) {
     const int hi = step / steps_per_head;
     const int i0 = key_start + (step - hi * steps_per_head) * kBMQ;
     const int h = h0 + hi;
-    const int buf = step % kStages;
     const long long head_off = (long long)b * s.N * q_row + (long long)h * D;
     const uint16_t* qt = contig_tile(a.q + head_off, q_row, base, i0, kBMQ, s.G, s.N);
     if (qt != nullptr) {
-      ts.load_contig(qt, Qs[buf], wave);
-      ts.load_contig(a.dout + (qt - a.q), Os[buf], wave);
+      ts.load_contig(qt, qbuf(c), wave);
+      ts.load_contig(a.dout + (qt - a.q), obuf(c), wave);
     } else {
       auto rows = [&](const uint16_t* head0) {
         return [=, &s](int row) {
@@ -306,35 +349,19 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
           return head0 + orig_pos(base, i, s.N) * q_row;
         };
       };
-      ts.load_rows(rows(a.q + head_off), Qs[buf], wave, lane);
-      ts.load_rows(rows(a.dout + head_off), Os[buf], wave, lane);
+      ts.load_rows(rows(a.q + head_off), qbuf(c), wave, lane);
+      ts.load_rows(rows(a.dout + head_off), obuf(c), wave, lane);
     }
-  };
-  // Row statistics of a step (lse in log2 units, Delta), through VGPRs.
-  auto load_stats = [&](int step) {
-    if (tid < 2 * kBMQ) {
-      const int hi = step / steps_per_head;
-      const int i0 = key_start + (step - hi * steps_per_head) * kBMQ;
-      const int h = h0 + hi;
-      const int i = i0 + (tid & (kBMQ - 1));
-      const long long so = ((long long)b * s.H + h) * s.N;
-      if (tid < kBMQ)
-        stat = i < s.G ? a.lse[so + orig_pos(base, i, s.N)] * kLog2e : INFINITY;
-      else
-        stat = i < s.G ? a.delta[so + orig_pos(base, i, s.N)] : 0.f;
+    if (wave == 0) {
+      const int i = min(i0 + l32, s.G - 1);
+      const long long so = ((long long)b * s.H + h) * s.N + orig_pos(base, i, s.N);
+      dma4((hh ? a.delta : a.lse) + so, stats(c));
     }
-  };
-  auto store_stats = [&](int step) {
-    const int buf = step % kStages;
-    if (tid < kBMQ)
-      Lse2[buf][tid] = stat;
-    else if (tid < 2 * kBMQ)
-      Dlt[buf][tid - kBMQ] = stat;
   };
 
   // Row offset of a step inside its q head's block sequence, and whether a
   // step's rows can see any of this pair's keys / cross its diagonal.
-  auto step_i0 = [&](int step) {
+  auto step_i0 = [&](int step) __attribute__((always_inline)) {
     const int hi = step / steps_per_head;
     return key_start + (step - hi * steps_per_head) * kBMQ;
   };
@@ -342,17 +369,19 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
   // P wave: S = Q K^T (lane column = key, elements = rows
   // 8*(r/4) + 4*hh + r%4 of the step), P = exp2(S*c*log2e - lse*log2e),
   // publish P, dV^T += dO^T P.
-  auto p_step = [&](int step, auto mask_tag) {
+  auto p_step = [&](int step, auto mask_tag, auto c) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    const int buf = step % kStages;
+    const uint16_t* qt = qbuf(c);
+    const uint16_t* ot = obuf(c);
+    const float* st = stats(c);
     const int i0 = step_i0(step);
     f32x16 sc = zero16();
     {
       bf16x8 qa[2];
-      qa[0] = sw.row(Qs[buf], 0, 0);
+      qa[0] = sw.row(qt, 0, 0);
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
-        if (kk + 1 < D / 16) qa[(kk + 1) & 1] = sw.row(Qs[buf], 0, kk + 1);
+        if (kk + 1 < D / 16) qa[(kk + 1) & 1] = sw.row(qt, 0, kk + 1);
         sc = mfma32x32x16(qa[kk & 1], kvf[kk], sc);
       }
     }
@@ -360,12 +389,13 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const int row0 = 8 * r4 + 4 * hh;
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&Lse2[buf][row0]);
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&st[row0]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float pv = fast_exp2(sc[r4 * 4 + e] * a.scale_log2 - l4[e]);
+        float pv = fast_exp2(sc[r4 * 4 + e] * a.scale_log2 - l4[e] * kLog2e);
         if constexpr (MASK) {
-          if (kj > i0 + row0 + e) pv = 0.f;
+          const int row = i0 + row0 + e;
+          if (kj > row || row >= s.G) pv = 0.f;
         }
         p[r4 * 4 + e] = pv;
       }
@@ -379,7 +409,7 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
     for (int hf = 0; hf < 2; ++hf) {
       bf16x8 ofr[D / 32];
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) ofr[db] = sw.tr(Os[buf], hf * 16, db);
+      for (int db = 0; db < D / 32; ++db) ofr[db] = sw.tr(ot, hf * 16, db);
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) acc[db] = mfma32x32x16(ofr[db], pb[hf], acc[db]);
     }
@@ -387,15 +417,17 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
 
   // dS wave (one step behind): dP = dO V^T, dS = P (dP - Delta) with the P
   // wave's published P, dK^T += Q^T dS.
-  auto ds_step = [&](int step) {
-    const int buf = step % kStages;
+  auto ds_step = [&](int step, auto c) __attribute__((always_inline)) {
+    const uint16_t* qt = qbuf(c);
+    const uint16_t* ot = obuf(c);
+    const float* st = stats(c);
     f32x16 dp = zero16();
     {
       bf16x8 oa[2];
-      oa[0] = sw.row(Os[buf], 0, 0);
+      oa[0] = sw.row(ot, 0, 0);
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
-        if (kk + 1 < D / 16) oa[(kk + 1) & 1] = sw.row(Os[buf], 0, kk + 1);
+        if (kk + 1 < D / 16) oa[(kk + 1) & 1] = sw.row(ot, 0, kk + 1);
         dp = mfma32x32x16(oa[kk & 1], kvf[kk], dp);
       }
     }
@@ -405,7 +437,7 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const int row0 = 8 * r4 + 4 * hh;
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&Dlt[buf][row0]);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&st[kBMQ + row0]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = r4 * 4 + e;
@@ -420,54 +452,58 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
     for (int hf = 0; hf < 2; ++hf) {
       bf16x8 qfr[D / 32];
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) qfr[db] = sw.tr(Qs[buf], hf * 16, db);
+      for (int db = 0; db < D / 32; ++db) qfr[db] = sw.tr(qt, hf * 16, db);
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) acc[db] = mfma32x32x16(qfr[db], dsb[hf], acc[db]);
     }
   };
 
   // Per q head: steps whose rows all precede this pair's keys contribute
-  // nothing and are skipped, the step crossing the diagonal is masked.
+  // nothing and are skipped; the step crossing the diagonal, and a last step
+  // that runs past the group end, are masked.
   const int skip = min(steps_per_head, (kw0 - key_start) / kBMQ);
   const int diag_end = min(steps_per_head, (kw0 + 31 - key_start) / kBMQ + 1);
-  auto step_kind = [&](int step) {  // 0 skip, 1 masked, 2 full
+  const int ragged = ((s.G - key_start) % kBMQ) != 0 ? steps_per_head - 1 : steps_per_head;
+  auto step_kind = [&](int step) __attribute__((always_inline)) {  // 0 skip, 1 masked, 2 full
     const int j = step % steps_per_head;
-    return j < skip ? 0 : (j < diag_end ? 1 : 2);
+    return j < skip ? 0 : ((j < diag_end || j >= ragged) ? 1 : 2);
   };
 
-  // Order per iteration: the statistics load for step n+1 is issued before
-  // the tile loads of step n+2, so waiting for it (to store it) and waiting
-  // for step n+1's tiles both leave step n+2's loads in flight.
-  const int loads_per_step = 2 * TileStage::count(wave);
-  if (nsteps > 0) {
-    load_stats(0);
-    load_step(0);
-    if (nsteps > 1) load_step(1);
-    store_stats(0);
-  }
+  const int loads_per_step = 2 * TileStage::count(wave) + (wave == 0 ? 1 : 0);
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
+  if (nsteps > 0) load_step(0, S0{});
+  if (nsteps > 1) load_step(1, S1{});
   wait_vmcnt_dyn(nsteps > 1 ? loads_per_step : 0);
-  __syncthreads();
+  lds_barrier();
 
-  // Iteration n: the P wave does step n, the dS wave step n-1; step n+1 is
-  // resident, step n+2 loads into the buffer that held step n-2.
-  // nsteps+1 iterations in all, identical for every wave.
-  for (int n = 0; n <= nsteps; ++n) {
-    if (n + 1 < nsteps) load_stats(n + 1);
-    if (n + 2 < nsteps) load_step(n + 2);
+  // Iteration n (stage c = n & 3): the P wave does step n, the dS wave step
+  // n-1; step n+1 is resident, step n+2 loads into the stage that held step
+  // n-2.  nsteps+1 iterations in all, identical for every wave.
+  auto iter = [&](int n, auto c) __attribute__((always_inline)) {
+    constexpr int C = decltype(c)::value;
+    if (n + 2 < nsteps) load_step(n + 2, std::integral_constant<int, (C + 2) & 3>{});
     if (!ds_wave) {
       if (n < nsteps) {
         const int kind = step_kind(n);
         if (kind == 2)
-          p_step(n, std::false_type{});
+          p_step(n, std::false_type{}, c);
         else if (kind == 1)
-          p_step(n, std::true_type{});
+          p_step(n, std::true_type{}, c);
       }
     } else {
-      if (n >= 1 && step_kind(n - 1) != 0) ds_step(n - 1);
+      if (n >= 1 && step_kind(n - 1) != 0) ds_step(n - 1, std::integral_constant<int, (C + 3) & 3>{});
     }
-    if (n + 1 < nsteps) store_stats(n + 1);
     wait_vmcnt_dyn(n + 2 < nsteps ? loads_per_step : 0);
-    __syncthreads();
+    lds_barrier();
+  };
+  for (int n = 0; n <= nsteps; n += 4) {
+    iter(n, S0{});
+    if (n + 1 <= nsteps) iter(n + 1, S1{});
+    if (n + 2 <= nsteps) iter(n + 2, S2{});
+    if (n + 3 <= nsteps) iter(n + 3, S3{});
   }
 
   if (kvalid) {

@@ -31,22 +31,26 @@ namespace {
 constexpr int kBN = 64;
 constexpr float kLazy = 8.f;  // log2-domain slack before the softmax reference moves
 
-// VCOPY: V reaches LDS as a transposed copy through VGPRs (plain 16-byte
-// reads for O^T += V^T P^T); otherwise V is loaded straight into LDS and read
-// with the transposing LDS read.
-template <int D, int NW, bool ROPE, bool VCOPY>
+template <int D, int NW, bool ROPE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_kernel(FwdArgs a, RopeTable rope) {
   constexpr int BM = NW * 32;
   using TileStage = LdsStage<D, kBN, NW>;
-  using VtStage = TransposeStage<D, kBN, NW * 64>;
-  // Eight-wave workgroups (one per CU) keep three tiles in LDS and load two
-  // ahead; smaller ones (two per CU) keep two and load one ahead.  The VGPR
-  // transposed copy of V is always one tile ahead.
-  constexpr int NBUF = (NW >= 8 && !VCOPY) ? 3 : 2;
-  constexpr int VELEMS = VCOPY ? D * VtStage::TSTR : kBN * D;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[NBUF][kBN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[NBUF][VELEMS];
-  VtStage vts;
+  // Double-buffered K/V tiles as four distinct LDS objects, each chosen at
+  // compile time (tile n lives in buffer n & 1): the compiler can then tell
+  // the reads of the current tile from the direct loads filling the other
+  // buffer, and does not make the reads wait for the tile still in flight.
+  __shared__ __attribute__((aligned(16))) uint16_t Ks0[kBN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks1[kBN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs0[kBN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs1[kBN * D];
+  auto kbuf = [&](auto p) __attribute__((always_inline)) -> uint16_t* {
+    if constexpr (decltype(p)::value) return Ks1; else return Ks0;
+  };
+  auto vbuf = [&](auto p) __attribute__((always_inline)) -> uint16_t* {
+    if constexpr (decltype(p)::value) return Vs1; else return Vs0;
+  };
+  using P0 = std::false_type;
+  using P1 = std::true_type;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep it scalar
@@ -103,36 +107,28 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // K and V tiles go straight from global memory into the swizzled LDS
   // tiles; rows past the group end point at the group's last row (their
   // keys are masked, so the values never contribute).
-  auto load_tile = [&](int n) {
+  auto load_tile = [&](int n, auto p) __attribute__((always_inline)) {
     const int key0 = n * kBN;
-    const int buf = n % NBUF;
     const uint16_t* kt = contig_tile(kb_ptr, kv_row, base, key0, kBN, s.G, s.N);
-    auto rows = [&](const uint16_t* head0) {
-      return [=, &s](int row) {
-        const int j = min(key0 + row, s.G - 1);
-        return head0 + orig_pos(base, j, s.N) * kv_row;
-      };
-    };
     if (kt != nullptr) {
-      ts.load_contig(kt, Ks[buf], wave);
-      if constexpr (VCOPY)
-        vts.load_contig(tid, vb_ptr + (kt - kb_ptr), (int)kv_row);
-      else
-        ts.load_contig(vb_ptr + (kt - kb_ptr), Vs[buf], wave);
+      ts.load_contig(kt, kbuf(p), wave);
+      ts.load_contig(vb_ptr + (kt - kb_ptr), vbuf(p), wave);
     } else {
-      ts.load_rows(rows(kb_ptr), Ks[buf], wave, lane);
-      if constexpr (VCOPY)
-        vts.load_rows(tid, rows(vb_ptr));
-      else
-        ts.load_rows(rows(vb_ptr), Vs[buf], wave, lane);
+      auto rows = [&](const uint16_t* head0) {
+        return [=, &s](int row) {
+          const int j = min(key0 + row, s.G - 1);
+          return head0 + orig_pos(base, j, s.N) * kv_row;
+        };
+      };
+      ts.load_rows(rows(kb_ptr), kbuf(p), wave, lane);
+      ts.load_rows(rows(vb_ptr), vbuf(p), wave, lane);
     }
   };
 
   // One k/v tile: S^T = K Q^T, online softmax, O^T += V^T P^T.  MASK is set
   // only for tiles that reach past this wave's first row (the diagonal).
-  auto compute = [&](int n, auto mask_tag) {
+  auto compute = [&](int n, auto mask_tag, auto p) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    const int cur = n % NBUF;
     const int key0 = n * kBN;
     // S^T: the two 32-key blocks are independent accumulators, interleaved
     // so back-to-back MFMAs never wait on each other; K fragments are read
@@ -141,7 +137,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
     for (int kb = 0; kb < kBN / 32; ++kb) sc[kb] = zero16();
     {
-      const uint16_t* kt = Ks[cur];
+      const uint16_t* kt = kbuf(p);
       bf16x8 kf[2][kBN / 32];
 #pragma unroll
       for (int kb = 0; kb < kBN / 32; ++kb) kf[0][kb] = sw.row(kt, kb * 32, 0);
@@ -207,22 +203,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // cycled in the inner loop; V^T fragments come from the row-major V tile
     // through the transposing read, one step ahead.
     {
-      const uint16_t* vt = Vs[cur];
+      const uint16_t* vt = vbuf(p);
       constexpr int KS = kBN / 16;  // 16-key reduction steps per tile
-      auto vfrag = [&](int ks, int db) -> bf16x8 {
-        if constexpr (VCOPY)
-          return lds_frag(vt + (db * 32 + l32) * VtStage::TSTR + ks * 16 + hh * 8);
-        else
-          return sw.tr(vt, ks * 16, db);
-      };
       bf16x8 vf[2][D / 32];
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) vf[0][db] = vfrag(0, db);
+      for (int db = 0; db < D / 32; ++db) vf[0][db] = sw.tr(vt, 0, db);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         if (ks + 1 < KS) {
 #pragma unroll
-          for (int db = 0; db < D / 32; ++db) vf[(ks + 1) & 1][db] = vfrag(ks + 1, db);
+          for (int db = 0; db < D / 32; ++db) vf[(ks + 1) & 1][db] = sw.tr(vt, (ks + 1) * 16, db);
         }
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
@@ -231,39 +221,36 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
   };
 
-  // Tile n+1 must have landed before the barrier that ends step n; the
-  // loads of later tiles may stay in flight.
-  const int loads_per_tile = (VCOPY ? 1 : 2) * TileStage::count(wave);
-  auto step = [&](int n, auto mask_tag) {
-    if (n + NBUF - 1 < ntiles) load_tile(n + NBUF - 1);
-    compute(n, mask_tag);
-    if constexpr (VCOPY) {
-      if (n + 1 < ntiles) vts.store(tid, Vs[(n + 1) % NBUF]);
-      wait_vmem_all();
-    } else {
-      wait_vmcnt_dyn(loads_per_tile * (min(n + NBUF - 1, ntiles - 1) - (n + 1)));
+  // Step n: start loading tile n+1 into the other buffer, compute tile n,
+  // then wait for tile n+1 and meet at the barrier (after which buffer n & 1
+  // may be overwritten).
+  auto step = [&](int n, auto mask_tag, auto p) __attribute__((always_inline)) {
+    if (n + 1 < ntiles) load_tile(n + 1, std::integral_constant<bool, !decltype(p)::value>{});
+    compute(n, mask_tag, p);
+    wait_vmem_all();
+    lds_barrier();
+  };
+  // Steps n0 .. n1-1, unrolled by two so each names its buffer statically.
+  auto run = [&](int n, int n1, auto mask_tag) __attribute__((always_inline)) {
+    if (n < n1 && (n & 1)) step(n++, mask_tag, P1{});
+    for (; n + 1 < n1; n += 2) {
+      step(n, mask_tag, P0{});
+      step(n + 1, mask_tag, P1{});
     }
-    __syncthreads();
+    if (n < n1) step(n, mask_tag, P0{});
   };
 
-#pragma unroll
-  for (int t = 0; t < NBUF - 1; ++t)
-    if (t < ntiles) load_tile(t);
-  if constexpr (VCOPY) {
-    vts.store(tid, Vs[0]);
-    wait_vmem_all();
-  } else {
-    wait_vmcnt_dyn(loads_per_tile * (min(NBUF - 2, ntiles - 1)));
-  }
-  __syncthreads();
+  load_tile(0, P0{});
+  wait_vmem_all();
+  lds_barrier();
 
   // Tiles whose keys all precede this wave's first row need no mask; the
   // rest (the diagonal, and for the lower waves of the tile one tile wholly
   // above them, which the mask zeroes) do.  Every wave runs ntiles steps, so
   // the barriers match.
   const int n_full = min(ntiles, (wave_q0 + 1) / kBN);
-  for (int n = 0; n < n_full; ++n) step(n, std::false_type{});
-  for (int n = n_full; n < ntiles; ++n) step(n, std::true_type{});
+  run(0, n_full, std::false_type{});
+  run(n_full, ntiles, std::true_type{});
 
   // ---- epilogue: normalise, write O and LSE at the original position ----
   const float lt = half_sum(l_run);
@@ -286,9 +273,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #ifndef S2A_FWD_WAVES_LARGE
 #define S2A_FWD_WAVES_LARGE 4  // waves per workgroup for groups longer than 1024
 #endif
-#ifndef S2A_FWD_VCOPY
-#define S2A_FWD_VCOPY 0  // V through a VGPR transposed copy (1) or transposing reads (0)
-#endif
 
 template <int D, int NW, bool ROPE>
 hipError_t launch_fwd_t(FwdArgs a, const RopeTable* rope, hipStream_t stream) {
@@ -299,7 +283,7 @@ hipError_t launch_fwd_t(FwdArgs a, const RopeTable* rope, hipStream_t stream) {
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   RopeTable rt{};
   if (ROPE) rt = *rope;
-  hipLaunchKernelGGL((fwd_kernel<D, NW, ROPE, S2A_FWD_VCOPY != 0>), dim3((unsigned)grid), dim3(NW * 64), 0, stream,
+  hipLaunchKernelGGL((fwd_kernel<D, NW, ROPE>), dim3((unsigned)grid), dim3(NW * 64), 0, stream,
                      a, rt);
   return hipGetLastError();
 }

@@ -83,6 +83,13 @@ struct LdsStage {
   }
 };
 
+// Direct global -> LDS load of 4 bytes per lane: lane l's word lands at
+// dst + 4*l bytes (dst is wave-uniform).
+__device__ __forceinline__ void dma4(const float* src, float* dst) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
+}
+
 // s_waitcnt on vmcnt only: wait until at most N of this wave's global loads
 // (LDS DMA included) are outstanding.  gfx9 immediate: vmcnt in bits 3:0 and
 // 15:14, expcnt 6:4 and lgkmcnt 11:8 set to their maxima (no wait).
@@ -93,6 +100,14 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 __device__ __forceinline__ void wait_vmem_all() { wait_vmcnt<0>(); }
+
+// Workgroup barrier for LDS hand-overs: completes this wave's LDS accesses
+// (lgkmcnt) and meets the other waves.  Unlike __syncthreads() it does not
+// drain outstanding global loads (a workgroup fence waits for them, direct-
+// to-LDS loads included), so loads of later tiles stay in flight across it;
+// callers first wait (vmcnt) for the tile the next step reads.  The "memory"
+// clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // wait_vmcnt for a wave-uniform count known only at run time (0..8).
 __device__ __forceinline__ void wait_vmcnt_dyn(int n) {
@@ -108,84 +123,6 @@ __device__ __forceinline__ void wait_vmcnt_dyn(int n) {
     default: wait_vmcnt<0>(); break;
   }
 }
-
-// Transposed copy through VGPRs: the R x D tile is written to LDS as
-// [D][R + 8] (row = column of the source), each 16-row block of a row in the
-// order tr_slot() gives, so a plain 16-byte read hands a lane the 8 rows
-// (in C-accumulator order) of one column.  Items are (4-row quad, 8-column
-// octet) blocks, quad index fastest: a thread owns 4 rows x 8 columns and
-// writes 8 columns x 4 rows as 8-byte words.  Costs VALU (v_perm) and 16
-// VGPRs per item but replaces the transposing read, which moves half the
-// bytes per cycle of a plain read.
-__device__ __forceinline__ int tr_slot(int j16) {
-  const int q = j16 >> 2;
-  return (((q & 1) << 3) | ((q & 2) << 1)) + (j16 & 3);
-}
-
-__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
-__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
-
-template <int D, int R, int NT>
-struct TransposeStage {
-  static constexpr int CH = D / 8;
-  static constexpr int NQ = R / 4;
-  static constexpr int ITEMS = NQ * CH;
-  static constexpr int PER = (ITEMS + NT - 1) / NT;
-  static constexpr int TSTR = R + 8;  // transposed row stride (elements)
-  u32x4 r[PER][4];
-
-  // R consecutive rows from `tile0`, `row_stride` elements apart.
-  __device__ __forceinline__ void load_contig(int tid, const uint16_t* tile0, int row_stride) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int item = tid + i * NT;
-      if (ITEMS % NT == 0 || item < ITEMS) {
-        const int rq = item % NQ, oc = item / NQ;
-        const int off = rq * 4 * row_stride + oc * 8;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) r[i][u] = ld16(tile0 + u * row_stride + off);
-      }
-    }
-  }
-
-  // General rows; `row_ptr(row)` returns a readable row (see LdsStage).
-  template <class RowPtr>
-  __device__ __forceinline__ void load_rows(int tid, RowPtr row_ptr) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int item = tid + i * NT;
-      if (ITEMS % NT == 0 || item < ITEMS) {
-        const int rq = item % NQ, oc = item / NQ;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) r[i][u] = ld16(row_ptr(rq * 4 + u) + oc * 8);
-      }
-    }
-  }
-
-  __device__ __forceinline__ void store(int tid, uint16_t* tr_lds) const {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int item = tid + i * NT;
-      if (ITEMS % NT == 0 || item < ITEMS) {
-        const int rq = item % NQ, oc = item / NQ;
-        const int pos = (rq >> 2) * 16 + tr_slot((rq & 3) * 4);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int w = e >> 1;
-          u32x2 pr;
-          if (e & 1) {
-            pr[0] = pack_hi(r[i][0][w], r[i][1][w]);
-            pr[1] = pack_hi(r[i][2][w], r[i][3][w]);
-          } else {
-            pr[0] = pack_lo(r[i][0][w], r[i][1][w]);
-            pr[1] = pack_lo(r[i][2][w], r[i][3][w]);
-          }
-          *reinterpret_cast<u32x2*>(tr_lds + (oc * 8 + e) * TSTR + pos) = pr;
-        }
-      }
-    }
-  }
-};
 
 // Start of a tile of R local rows beginning at local row j0 of a group whose
 // first rolled row is at original position `base`, if those R rows are R
