@@ -74,10 +74,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // Double-buffered K/V tiles as distinct LDS objects named at compile time
   // (tile n in buffer n & 1), so reads of one buffer never wait for the
   // direct loads into the other.
-  __shared__ __attribute__((aligned(16))) uint16_t Ks0[kBN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Ks1[kBN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs0[kBN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs1[kBN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks0[TileStage::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks1[TileStage::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs0[TileStage::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs1[TileStage::ELEMS];
   auto kbuf = [&](auto p) __attribute__((always_inline)) -> uint16_t* {
     if constexpr (decltype(p)::value) return Ks1; else return Ks0;
   };
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep it scalar
   const int lane = tid & 63;
   const int l32 = lane & 31, hh = lane >> 5;
-  const SwzLane<D> sw(lane);
+  const TileLane<D> sw(lane);
   const Shape& s = a.s;
 
   const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
@@ -181,7 +181,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       for (int r = 0; r < 16; ++r) {
         float p = fast_exp2(sc[r] * a.scale_log2 - lse2);
         if constexpr (MASK) {
-          const int j = key0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+          const int j = key0 + kb * 32 + acc_row(r, hh);
           if (j > qi) p = 0.f;
         }
         ds[r] = p * (dp[r] - dlt);
@@ -255,12 +255,12 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
   // The ring's q and dout tiles are eight distinct LDS objects, each named
   // at compile time (step m in stage m & 3), so reads of one stage never
   // wait for the direct loads into another.
-  __shared__ __attribute__((aligned(16))) uint16_t Q0[kBMQ * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Q1[kBMQ * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Q2[kBMQ * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Q3[kBMQ * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Q0[TileStage::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t Q1[TileStage::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t Q2[TileStage::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t Q3[TileStage::ELEMS];
   // dout tile, then the step's 32 lse values and 32 Delta values (fp32).
-  constexpr int kOElems = kBMQ * D + 2 * kBMQ * 2;
+  constexpr int kOElems = TileStage::ELEMS + 2 * kBMQ * 2;
   __shared__ __attribute__((aligned(16))) uint16_t O0[kOElems];
   __shared__ __attribute__((aligned(16))) uint16_t O1[kOElems];
   __shared__ __attribute__((aligned(16))) uint16_t O2[kOElems];
@@ -283,7 +283,7 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep it scalar
   const int lane = tid & 63;
   const int l32 = lane & 31, hh = lane >> 5;
-  const SwzLane<D> sw(lane);
+  const TileLane<D> sw(lane);
   const bool ds_wave = wave >= kDkdvPairs;
   const int pair = wave & (kDkdvPairs - 1);
   const Shape& s = a.s;
@@ -327,7 +327,7 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
 
   const TileStage ts(wave, lane, (int)q_row);
   auto stats = [&](auto c) __attribute__((always_inline)) -> float* {
-    return reinterpret_cast<float*>(obuf(c) + kBMQ * D);
+    return reinterpret_cast<float*>(obuf(c) + TileStage::ELEMS);
   };
   // q and dout rows of a step go straight into LDS, and wave 0 loads the
   // rows' lse (lanes 0-31) and Delta (lanes 32-63) behind the dout tile.
@@ -353,7 +353,7 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
       ts.load_rows(rows(a.dout + head_off), obuf(c), wave, lane);
     }
     if (wave == 0) {
-      const int i = min(i0 + l32, s.G - 1);
+      const int i = min(i0 + rowperm32(l32), s.G - 1);  // slot m holds tile row rowperm32(m)
       const long long so = ((long long)b * s.H + h) * s.N + orig_pos(base, i, s.N);
       dma4((hh ? a.delta : a.lse) + so, stats(c));
     }
@@ -394,7 +394,7 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
       for (int e = 0; e < 4; ++e) {
         float pv = fast_exp2(sc[r4 * 4 + e] * a.scale_log2 - l4[e] * kLog2e);
         if constexpr (MASK) {
-          const int row = i0 + row0 + e;
+          const int row = i0 + acc_row(4 * r4 + e, hh);
           if (kj > row || row >= s.G) pv = 0.f;
         }
         p[r4 * 4 + e] = pv;

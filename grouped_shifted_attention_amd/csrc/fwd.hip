@@ -35,28 +35,32 @@ template <int D, int NW, bool ROPE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_kernel(FwdArgs a, RopeTable rope) {
   constexpr int BM = NW * 32;
   using TileStage = LdsStage<D, kBN, NW>;
-  // Double-buffered K/V tiles as four distinct LDS objects, each chosen at
-  // compile time (tile n lives in buffer n & 1): the compiler can then tell
-  // the reads of the current tile from the direct loads filling the other
-  // buffer, and does not make the reads wait for the tile still in flight.
-  __shared__ __attribute__((aligned(16))) uint16_t Ks0[kBN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Ks1[kBN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs0[kBN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs1[kBN * D];
-  auto kbuf = [&](auto p) __attribute__((always_inline)) -> uint16_t* {
-    if constexpr (decltype(p)::value) return Ks1; else return Ks0;
+  // K/V tile ring of NBUF stages (tile n in stage n % NBUF), each stage two
+  // distinct LDS objects named at compile time: the compiler can then tell
+  // the reads of one stage from the direct loads filling another and does
+  // not make the reads wait for tiles still in flight.  Eight-wave
+  // workgroups (one per CU) afford three stages, so a tile's loads are
+  // issued two steps before it is read; four-wave ones (two per CU) two.
+  constexpr int NBUF = NW >= 8 ? 3 : 2;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks0[TileStage::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks1[TileStage::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks2[NBUF > 2 ? TileStage::ELEMS : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs0[TileStage::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs1[TileStage::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs2[NBUF > 2 ? TileStage::ELEMS : 8];
+  auto kbuf = [&](auto c) __attribute__((always_inline)) -> uint16_t* {
+    constexpr int C = decltype(c)::value;
+    if constexpr (C == 0) return Ks0; else if constexpr (C == 1) return Ks1; else return Ks2;
   };
-  auto vbuf = [&](auto p) __attribute__((always_inline)) -> uint16_t* {
-    if constexpr (decltype(p)::value) return Vs1; else return Vs0;
+  auto vbuf = [&](auto c) __attribute__((always_inline)) -> uint16_t* {
+    constexpr int C = decltype(c)::value;
+    if constexpr (C == 0) return Vs0; else if constexpr (C == 1) return Vs1; else return Vs2;
   };
-  using P0 = std::false_type;
-  using P1 = std::true_type;
-
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep it scalar
   const int lane = tid & 63;
   const int l32 = lane & 31, hh = lane >> 5;
-  const SwzLane<D> sw(lane);
+  const TileLane<D> sw(lane);
   const Shape& s = a.s;
 
   // Work item: heavy (long causal rows) tiles first within a unit; units
@@ -81,24 +85,30 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const bool qvalid = qi < s.G;
   const int qpos = qvalid ? orig_pos(base, qi, s.N) : 0;
   const long long qoff = ((long long)(b * (long long)s.N + qpos) * s.H + h) * D;
+  // The softmax scale and log2(e) are folded into q once (one bf16
+  // rounding of q * scale * log2 e), so S^T comes out of the MFMA in log2
+  // units and P = exp2(S - m) needs no multiply.
   bf16x8 qf[D / 16];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
-    u32x4 raw = qvalid ? ld16(a.q + qoff + kk * 16 + hh * 8) : zero_u4();
-    if constexpr (ROPE) {
-      float x[8];
-      unpack8(raw, x);
-      rope_rotate8(x, qpos, rope.rev, kk * 16 + hh * 8, false);
-      raw = pack8(x);
-    }
-    qf[kk] = as_bf16x8(raw);
+    const u32x4 raw = qvalid ? ld16(a.q + qoff + kk * 16 + hh * 8) : zero_u4();
+    float x[8];
+    unpack8(raw, x);
+    if constexpr (ROPE) rope_rotate8(x, qpos, rope.rev, kk * 16 + hh * 8, false);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] *= a.scale_log2;
+    qf[kk] = as_bf16x8(pack8(x));
   }
 
   f32x16 o[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) o[i] = zero16();
-  float m_run = -INFINITY;  // running max of scaled logits (log2 domain)
-  float l_run = 0.f;        // this lane's half of the running row sum
+  // Softmax reference m_run (log2 units, -inf before the first tile).  The
+  // S^T accumulators start at s0 = -m_run (0 before the first tile), so the
+  // MFMA hands back S - m_run and P = exp2 of it.
+  float m_run = -INFINITY;
+  f32x16 s0 = zero16();
+  float l_run = 0.f;  // this lane's half of the running row sum
 
   const int rows_end = min((t + 1) * BM, s.G);
   const int ntiles = (rows_end + kBN - 1) / kBN;
@@ -107,12 +117,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // K and V tiles go straight from global memory into the swizzled LDS
   // tiles; rows past the group end point at the group's last row (their
   // keys are masked, so the values never contribute).
-  auto load_tile = [&](int n, auto p) __attribute__((always_inline)) {
+  auto load_tile = [&](int n, auto c) __attribute__((always_inline)) {
     const int key0 = n * kBN;
     const uint16_t* kt = contig_tile(kb_ptr, kv_row, base, key0, kBN, s.G, s.N);
     if (kt != nullptr) {
-      ts.load_contig(kt, kbuf(p), wave);
-      ts.load_contig(vb_ptr + (kt - kb_ptr), vbuf(p), wave);
+      ts.load_contig(kt, kbuf(c), wave);
+      ts.load_contig(vb_ptr + (kt - kb_ptr), vbuf(c), wave);
     } else {
       auto rows = [&](const uint16_t* head0) {
         return [=, &s](int row) {
@@ -120,15 +130,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
           return head0 + orig_pos(base, j, s.N) * kv_row;
         };
       };
-      ts.load_rows(rows(kb_ptr), kbuf(p), wave, lane);
-      ts.load_rows(rows(vb_ptr), vbuf(p), wave, lane);
+      ts.load_rows(rows(kb_ptr), kbuf(c), wave, lane);
+      ts.load_rows(rows(vb_ptr), vbuf(c), wave, lane);
     }
   };
 
-  // One k/v tile: S^T = K Q^T, online softmax, O^T += V^T P^T.  MASK is set
-  // only for tiles that reach past this wave's first row (the diagonal).
-  auto compute = [&](int n, auto mask_tag, auto p) __attribute__((always_inline)) {
-    constexpr bool MASK = decltype(mask_tag)::value;
+  // Tiles whose keys all precede this wave's first row need no mask; the
+  // rest (the diagonal, and for the lower waves of the tile one tile wholly
+  // above them, which the mask zeroes) do.
+  const int n_full = min(ntiles, (wave_q0 + 1) / kBN);
+
+  // One k/v tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
+  auto compute = [&](int n, auto c) __attribute__((always_inline)) {
     const int key0 = n * kBN;
     // S^T: the two 32-key blocks are independent accumulators, interleaved
     // so back-to-back MFMAs never wait on each other; K fragments are read
@@ -137,54 +150,78 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
     for (int kb = 0; kb < kBN / 32; ++kb) sc[kb] = zero16();
     {
-      const uint16_t* kt = kbuf(p);
-      bf16x8 kf[2][kBN / 32];
+      const uint16_t* kt = kbuf(c);
+      constexpr int KD = 3;  // K fragments in flight: reads run two k-steps ahead
+      bf16x8 kf[KD][kBN / 32];
 #pragma unroll
-      for (int kb = 0; kb < kBN / 32; ++kb) kf[0][kb] = sw.row(kt, kb * 32, 0);
+      for (int kk = 0; kk < KD - 1; ++kk)
+#pragma unroll
+        for (int kb = 0; kb < kBN / 32; ++kb) kf[kk][kb] = sw.row(kt, kb * 32, kk);
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) {
-        if (kk + 1 < D / 16) {
+        if (kk + KD - 1 < D / 16) {
 #pragma unroll
           for (int kb = 0; kb < kBN / 32; ++kb)
-            kf[(kk + 1) & 1][kb] = sw.row(kt, kb * 32, kk + 1);
+            kf[(kk + KD - 1) % KD][kb] = sw.row(kt, kb * 32, kk + KD - 1);
         }
 #pragma unroll
-        for (int kb = 0; kb < kBN / 32; ++kb) sc[kb] = mfma32x32x16(kf[kk & 1][kb], qf[kk], sc[kb]);
+        for (int kb = 0; kb < kBN / 32; ++kb) sc[kb] = mfma32x32x16(kf[kk % KD][kb], qf[kk], kk == 0 ? s0 : sc[kb]);
+      }
+      // Keep the K reads (KD-1) k-steps ahead of the MFMAs that use them:
+      // the scheduler would otherwise sink each read next to its use and
+      // expose the LDS latency.
+      constexpr int NB = kBN / 32;
+      __builtin_amdgcn_sched_group_barrier(0x100, (KD - 1) * NB, 0);
+#pragma unroll
+      for (int i = 0; i < (D / 16) * NB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i < (D / 16 - (KD - 1)) * NB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
     }
-    if constexpr (MASK) {
+    if (n >= n_full) {
 #pragma unroll
       for (int kb = 0; kb < kBN / 32; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int j = key0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+          const int j = key0 + kb * 32 + acc_row(r, hh);
           if (j > qi) sc[kb][r] = -INFINITY;
         }
     }
     // Online softmax in the exp2 domain with a lazily moved reference: the
-    // accumulators are rescaled only when some row's max exceeds the current
-    // reference by more than kLazy (so p <= 2^kLazy); otherwise the stale
-    // reference stays, which changes nothing in exact arithmetic.
+    // reference moves (and O, l are rescaled) only when some row's max
+    // exceeds it by more than kLazy (so p <= 2^kLazy), and on the first
+    // tile; otherwise the stale reference stays, which changes nothing in
+    // exact arithmetic.
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < kBN / 32; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
-    mx = half_max(mx) * a.scale_log2;
-    if (__any(mx > m_run + kLazy)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = fast_exp2(m_run - m_new);
+    mx = half_max(mx);  // relative to m_run (absolute before the first tile)
+    const bool first = m_run == -INFINITY;
+    if (__any(mx > kLazy || first)) {
+      float m_new = first ? mx : m_run + fmaxf(mx, 0.f);
+      if (mx == -INFINITY) m_new = m_run;  // nothing visible yet
+      const float alpha = m_new == m_run ? 1.f : fast_exp2(m_run - m_new);
+      const float shift = m_new == -INFINITY ? 0.f : m_new - (first ? 0.f : m_run);
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < D / 32; ++i) o[i] *= alpha;
+#pragma unroll
+      for (int kb = 0; kb < kBN / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[kb][r] -= shift;
+      const float neg = m_run == -INFINITY ? 0.f : -m_run;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s0[r] = neg;
     }
     float rs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < kBN / 32; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float pv = fast_exp2(sc[kb][r] * a.scale_log2 - m_run);
+        const float pv = fast_exp2(sc[kb][r]);
         sc[kb][r] = pv;
         rs += pv;
       }
@@ -203,7 +240,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // cycled in the inner loop; V^T fragments come from the row-major V tile
     // through the transposing read, one step ahead.
     {
-      const uint16_t* vt = vbuf(p);
+      const uint16_t* vt = vbuf(c);
       constexpr int KS = kBN / 16;  // 16-key reduction steps per tile
       bf16x8 vf[2][D / 32];
 #pragma unroll
@@ -221,36 +258,34 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
   };
 
-  // Step n: start loading tile n+1 into the other buffer, compute tile n,
-  // then wait for tile n+1 and meet at the barrier (after which buffer n & 1
-  // may be overwritten).
-  auto step = [&](int n, auto mask_tag, auto p) __attribute__((always_inline)) {
-    if (n + 1 < ntiles) load_tile(n + 1, std::integral_constant<bool, !decltype(p)::value>{});
-    compute(n, mask_tag, p);
-    wait_vmem_all();
+  // Step n (stage C = n % NBUF): start loading tile n + NBUF - 1 into the
+  // stage step n - 1 finished with, compute tile n, wait for tile n + 1
+  // (later tiles' loads stay in flight) and meet at the barrier.  Every wave
+  // runs ntiles steps, so the barriers match.
+  const int loads_per_tile = 2 * TileStage::count(wave);
+  auto step = [&](int n, auto c) __attribute__((always_inline)) {
+    constexpr int C = decltype(c)::value;
+    if (n + NBUF - 1 < ntiles) load_tile(n + NBUF - 1, std::integral_constant<int, (C + NBUF - 1) % NBUF>{});
+    compute(n, c);
+    wait_vmcnt_dyn(loads_per_tile * (min(n + NBUF - 1, ntiles - 1) - (n + 1)));
     lds_barrier();
   };
-  // Steps n0 .. n1-1, unrolled by two so each names its buffer statically.
-  auto run = [&](int n, int n1, auto mask_tag) __attribute__((always_inline)) {
-    if (n < n1 && (n & 1)) step(n++, mask_tag, P1{});
-    for (; n + 1 < n1; n += 2) {
-      step(n, mask_tag, P0{});
-      step(n + 1, mask_tag, P1{});
-    }
-    if (n < n1) step(n, mask_tag, P0{});
-  };
 
-  load_tile(0, P0{});
-  wait_vmem_all();
+#pragma unroll
+  for (int i = 0; i < NBUF - 1; ++i) {
+    if (i == 0) load_tile(0, std::integral_constant<int, 0>{});
+    if (i == 1 && ntiles > 1) load_tile(1, std::integral_constant<int, 1>{});
+  }
+  wait_vmcnt_dyn(loads_per_tile * (min(NBUF - 2, ntiles - 1)));
   lds_barrier();
 
-  // Tiles whose keys all precede this wave's first row need no mask; the
-  // rest (the diagonal, and for the lower waves of the tile one tile wholly
-  // above them, which the mask zeroes) do.  Every wave runs ntiles steps, so
-  // the barriers match.
-  const int n_full = min(ntiles, (wave_q0 + 1) / kBN);
-  run(0, n_full, std::false_type{});
-  run(n_full, ntiles, std::true_type{});
+  for (int n = 0; n < ntiles; n += NBUF) {
+    step(n, std::integral_constant<int, 0>{});
+    if (n + 1 < ntiles) step(n + 1, std::integral_constant<int, 1>{});
+    if constexpr (NBUF > 2) {
+      if (n + 2 < ntiles) step(n + 2, std::integral_constant<int, 2>{});
+    }
+  }
 
   // ---- epilogue: normalise, write O and LSE at the original position ----
   const float lt = half_sum(l_run);

@@ -2,51 +2,74 @@
 // LDS read helpers that turn them into MFMA operands.
 //
 // A tile is R rows x D columns of a [rows, heads, D] tensor whose rows are
-// gathered through the roll/group index map.  Tiles are loaded one step
-// ahead, straight into LDS, so global latency hides behind MFMA work.
+// gathered through the roll/group index map.  Tiles are loaded ahead of use,
+// straight into LDS, so global latency hides behind MFMA work.
 //
-// LDS layout: row-major [R][D] with the 16-byte chunks of each row XOR-
-// swizzled: logical chunk c of row r is stored at chunk c ^ swz(r),
-// swz(r) = 2*(r & 3) + ((r >> 2) & 1).  A row is an MFMA operand with k = d
-// (one 16-byte read per lane, 8 consecutive rows per read pass); a column
-// block is an MFMA operand with k = row through the transposing LDS read
-// (4 consecutive rows x 32 bytes per 16 lanes).  The swizzle puts both read
-// shapes, and the row writes, on distinct banks; no single row padding can.
+// LDS layout: row-major with one padding chunk (16 bytes) after every row,
+// i.e. a row stride of D + 8 elements, so successive rows start one bank
+// group (16 bytes = 4 of the 64 four-byte banks) further on.  Two read
+// shapes must be free of bank conflicts:
+//   row read (16 bytes per lane, 16 lanes per cycle): 16 tile rows, one
+//     chunk each -- conflict-free for any 16 rows distinct mod 16;
+//   transposing read (8 bytes per lane, 32 lanes per cycle): 4 tile rows x
+//     4 consecutive chunks x 2 halves -- conflict-free when the 4 rows are
+//     4 apart.
+// Both hold because each 16-row block of a tile is visited in the order
+//   rowperm(m) = 4*(m%4) + 2*(m/8) + (m/4)%2   (an involution),
+// i.e. MFMA operand row m of a 16-row block is tile row rowperm(m).  The
+// rows a C accumulator hands a lane (8*(r/4) + 4*hh + r%4, the reduction
+// order when that C tile is fed back as a B operand) then map to tile rows
+// 4*t + hh (elements 0-3) and 4*t + 2 + hh (elements 4-7): 4 apart, as the
+// transposing read wants.  All addresses stay a per-lane base plus
+// compile-time offsets.
 #pragma once
 
 #include "device_common.hpp"
 
 namespace s2a {
 
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+// Tile row of MFMA operand row m (0..31) of a 32-row block.
+__device__ __forceinline__ constexpr int rowperm32(int m) {
+  return (m & 16) | (((m & 3) << 2) | (((m >> 3) & 1) << 1) | ((m >> 2) & 1));
+}
+// Tile row of accumulator element r (0..15) of a lane in half hh of a
+// 32 x 32 C tile whose rows were produced from rowperm32-ordered operands.
+__device__ __forceinline__ constexpr int acc_row(int r, int hh) { return rowperm32(8 * (r >> 2) + 4 * hh + (r & 3)); }
 
 // Direct global -> LDS staging (global_load_lds_dwordx4) of an R x D tile
-// into the swizzled layout; no VGPRs hold the data.  One wave instruction
+// into the padded layout; no VGPRs hold the data.  One wave instruction
 // moves 64 lanes x 16 bytes into 1 KB of LDS, lane l's bytes at +16*l, so
-// instruction `inst` fills tile chunks 64*inst .. 64*inst+63, i.e. physical
-// chunk p = q % (D/8) of row q / (D/8); the lane fetches the logical chunk
-// p ^ swz(row) from global memory.  The NW waves of the workgroup split the
-// R*D/512 instructions round-robin.  Completion is tracked by vmcnt: wait
-// (s_waitcnt vmcnt) and barrier before the tile is read.
+// instruction `inst` fills slots 64*inst .. 64*inst+63 of the tile, slot q
+// being chunk q % (D/8 + 1) of row q / (D/8 + 1).  Lanes on a padding slot,
+// or past the last row, fetch a harmless in-bounds chunk (row clamped, chunk
+// 0) into LDS that is never read, so every lane of every instruction loads.
+// The NW waves of the workgroup split the instructions round-robin.
+// Completion is tracked by vmcnt: wait (s_waitcnt vmcnt) and barrier before
+// the tile is read.
 template <int D, int R, int NW>
 struct LdsStage {
   static constexpr int CH = D / 8;
-  static constexpr int INSTR = R * CH / 64;
+  static constexpr int RS = D + 8;               // LDS row stride (elements)
+  static constexpr int SLOTS = R * (CH + 1);
+  static constexpr int INSTR = (SLOTS + 63) / 64;
+  static constexpr int ELEMS = INSTR * 512;      // LDS elements a tile occupies
   static constexpr int PER = (INSTR + NW - 1) / NW;
-  static_assert(R * CH % 64 == 0, "tile must be a whole number of 1 KB wave loads");
   int off[PER];  // fast path: element offset of the lane's chunk in a contiguous tile
 
-  __device__ __forceinline__ static int chunk_row(int inst, int lane) { return (inst * 64 + lane) / CH; }
-  __device__ __forceinline__ static int chunk_col(int inst, int lane) {
+  __device__ __forceinline__ static int slot_row(int inst, int lane) {
+    return min((inst * 64 + lane) / (CH + 1), R - 1);
+  }
+  __device__ __forceinline__ static int slot_col(int inst, int lane) {
     const int q = inst * 64 + lane;
-    return ((q % CH) ^ swz(q / CH)) << 3;
+    const int c = q % (CH + 1);
+    return (q < SLOTS && c < CH) ? c << 3 : 0;
   }
 
   __device__ __forceinline__ LdsStage(int wave, int lane, int row_stride) {
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int inst = wave + k * NW;
-      off[k] = chunk_row(inst, lane) * row_stride + chunk_col(inst, lane);
+      off[k] = slot_row(inst, lane) * row_stride + slot_col(inst, lane);
     }
   }
 
@@ -78,7 +101,7 @@ struct LdsStage {
     for (int k = 0; k < PER; ++k) {
       const int inst = wave + k * NW;
       if (INSTR % NW == 0 || inst < INSTR)
-        dma(row_ptr(chunk_row(inst, lane)) + chunk_col(inst, lane), lds + inst * 512);
+        dma(row_ptr(slot_row(inst, lane)) + slot_col(inst, lane), lds + inst * 512);
     }
   }
 };
@@ -109,7 +132,8 @@ __device__ __forceinline__ void wait_vmem_all() { wait_vmcnt<0>(); }
 // clobber keeps the compiler from moving memory accesses across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// wait_vmcnt for a wave-uniform count known only at run time (0..8).
+// wait_vmcnt for a wave-uniform count known only at run time (0..16; larger
+// counts wait for everything, which is always safe).
 __device__ __forceinline__ void wait_vmcnt_dyn(int n) {
   switch (n) {
     case 1: wait_vmcnt<1>(); break;
@@ -120,6 +144,14 @@ __device__ __forceinline__ void wait_vmcnt_dyn(int n) {
     case 6: wait_vmcnt<6>(); break;
     case 7: wait_vmcnt<7>(); break;
     case 8: wait_vmcnt<8>(); break;
+    case 9: wait_vmcnt<9>(); break;
+    case 10: wait_vmcnt<10>(); break;
+    case 11: wait_vmcnt<11>(); break;
+    case 12: wait_vmcnt<12>(); break;
+    case 13: wait_vmcnt<13>(); break;
+    case 14: wait_vmcnt<14>(); break;
+    case 15: wait_vmcnt<15>(); break;
+    case 16: wait_vmcnt<16>(); break;
     default: wait_vmcnt<0>(); break;
   }
 }
@@ -153,44 +185,41 @@ __device__ __forceinline__ s16x4 lds_read_tr(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
 }
 
-// Per-lane addressing of the swizzled tiles, computed once per kernel.
+// Per-lane addressing of the padded tiles, computed once per kernel.
 //
-// Row read (MFMA operand with k = d): the lane's row is rb + lane%32 (rb a
-// multiple of 8), k-step kk covers logical chunk 2*kk + lane/32.  Because
-// swz() only touches the low 3 chunk bits and depends only on row % 8, the
-// offset is rb*D + 64*(kk/4) + row_off[kk%4].
+// Row read (MFMA operand with k = d): operand row m = lane%32 of a 32-row
+// block at tile row rb (a multiple of 32) is tile row rb + rowperm32(m);
+// k-step kk covers chunk 2*kk + lane/32.
 //
 // Transposed read (MFMA A operand with k = tile row): lane l belongs to group
-// g = l/16 (hh = g/2 picks the row half, g%2 the 16-column half) and has
-// i = l%16 (row i/4 of a 4-row block, 4-element column chunk i%4).  Element
-// s of a lane in half hh is row k0 + 8*(s/4) + 4*hh + s%4 (the order a C
-// accumulator hands a lane its rows) and its column is 32*db + lane%32; the
-// offset is k0*D + 64*(db/2) + tr_off[db%2] (+ 8*D for the second 4 rows).
+// g = l/16 (hh = g/2 picks the C-order half, g%2 the 16-column half) and has
+// i = l%16.  Lanes 4t..4t+3 of a group supply 4-column pieces of one tile
+// row, which the instruction hands out so that every lane receives one
+// column across the group's 4 rows.  For the 16-row block at k0 (a multiple
+// of 16) the lo read covers rows k0 + 4t + hh, the hi read rows
+// k0 + 4t + 2 + hh (t = 0..3), which are the tile rows of accumulator
+// elements 0-3 and 4-7 (see acc_row); the lane's column is 32*db + lane%32.
 template <int D>
-struct SwzLane {
-  int row_off[4];
-  int tr_off[2];
+struct TileLane {
+  static constexpr int RS = D + 8;
+  int rbase;  // row read: element offset of the lane's row and chunk
+  int tbase;  // transposed read: element offset of the lane's lo row piece
 
-  __device__ __forceinline__ explicit SwzLane(int lane) {
+  __device__ __forceinline__ explicit TileLane(int lane) {
     const int l32 = lane & 31, hh = lane >> 5;
-    const int y = hh ^ swz(l32 & 7);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) row_off[q] = l32 * D + (((2 * q) ^ y) << 3);
+    rbase = rowperm32(l32) * RS + hh * 8;
     const int g = lane >> 4, i = lane & 15;
-    const int r = 4 * (g >> 1) + (i >> 2);
-    const int lc = 2 * (g & 1) + ((i & 3) >> 1);
-#pragma unroll
-    for (int od = 0; od < 2; ++od) tr_off[od] = r * D + (((4 * od + lc) ^ swz(r)) << 3) + 4 * (i & 1);
+    tbase = (4 * (i >> 2) + (g >> 1)) * RS + (2 * (g & 1) + ((i & 3) >> 1)) * 8 + 4 * (i & 1);
   }
 
   __device__ __forceinline__ bf16x8 row(const uint16_t* tile, int rb, int kk) const {
-    return lds_frag(tile + rb * D + ((kk >> 2) << 6) + row_off[kk & 3]);
+    return lds_frag(tile + rb * RS + rbase + 16 * kk);
   }
 
   __device__ __forceinline__ bf16x8 tr(const uint16_t* tile, int k0, int db) const {
-    const uint16_t* p = tile + k0 * D + ((db >> 1) << 6) + tr_off[db & 1];
+    const uint16_t* p = tile + k0 * RS + tbase + 32 * db;
     const s16x4 lo = lds_read_tr(p);
-    const s16x4 hi = lds_read_tr(p + 8 * D);  // swz(r + 8) == swz(r)
+    const s16x4 hi = lds_read_tr(p + 2 * RS);
     typedef short s16x8 __attribute__((ext_vector_type(8)));
     const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return __builtin_bit_cast(bf16x8, v);
