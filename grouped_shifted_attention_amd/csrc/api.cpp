@@ -155,7 +155,8 @@ int do_bwd(const void* q, const void* k, const void* v, const void* out, const f
   if (rope && (st = check_rope(rope[0], rope[1]))) return st;
   if (B == 0 || N == 0) return S2ATTN_OK;
   const size_t qb = q_bytes(B, N, H, D), kb = q_bytes(B, N, Hkv, D), sb = stat_bytes(B, N, H);
-  const size_t need = rope ? round_up(sb) + round_up(qb) + round_up(kb) : round_up(sb);
+  const size_t stats = 2 * round_up(sb);  // -Delta, then -lse*log2(e)
+  const size_t need = rope ? stats + round_up(qb) + round_up(kb) : stats;
   Buf in[6] = {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"}, {out, qb, "out"}, {lse, sb, "lse"}, {dout, qb, "dout"}};
   Buf outs[4] = {{dq, qb, "dq"}, {dk, kb, "dk"}, {dv, kb, "dv"}, {ws, need, "workspace"}};
   st = check_buffers(in, 6, outs, 4);
@@ -164,14 +165,15 @@ int do_bwd(const void* q, const void* k, const void* v, const void* out, const f
   if (((uintptr_t)ws & (kAlign - 1)) != 0) return fail(S2ATTN_EINVAL, "workspace is not 256-byte aligned");
   const hipStream_t s = (hipStream_t)stream;
   char* w = (char*)ws;
-  float* delta = (float*)w;
+  float* ndelta = (float*)w;
+  float* nlse2 = (float*)(w + round_up(sb));
   s2a::BwdArgs a{};
   a.q = (const uint16_t*)q;
   a.k = (const uint16_t*)k;
   a.v = (const uint16_t*)v;
   a.dout = (const uint16_t*)dout;
-  a.lse = lse;
-  a.delta = delta;
+  a.nlse2 = nlse2;
+  a.ndelta = ndelta;
   a.dq = (uint16_t*)dq;
   a.dk = (uint16_t*)dk;
   a.dv = (uint16_t*)dv;
@@ -182,15 +184,16 @@ int do_bwd(const void* q, const void* k, const void* v, const void* out, const f
   s2a::RopeTable t{};
   if (rope) {
     t = make_rope(D, rope[0], rope[1]);
-    uint16_t* qrot = (uint16_t*)(w + round_up(sb));
-    uint16_t* krot = (uint16_t*)(w + round_up(sb) + round_up(qb));
+    uint16_t* qrot = (uint16_t*)(w + stats);
+    uint16_t* krot = (uint16_t*)(w + stats + round_up(qb));
     if ((e = s2a::launch_rope_rotate(a.q, qrot, a.s, H, t, s)) != hipSuccess) return hip_fail(e, "rope(q)");
     if ((e = s2a::launch_rope_rotate(a.k, krot, a.s, Hkv, t, s)) != hipSuccess) return hip_fail(e, "rope(k)");
     a.q = qrot;
     a.k = krot;
   }
-  if ((e = s2a::launch_bwd_delta((const uint16_t*)out, a.dout, delta, a.s, s)) != hipSuccess)
-    return hip_fail(e, "backward delta");
+  if ((e = s2a::launch_bwd_delta((const uint16_t*)out, (const uint16_t*)dout, lse, ndelta, nlse2, a.s, s)) !=
+      hipSuccess)
+    return hip_fail(e, "backward preprocess");
   if ((e = s2a::launch_bwd_dkdv(a, rope ? &t : nullptr, s)) != hipSuccess) return hip_fail(e, "backward dk/dv");
   if ((e = s2a::launch_bwd_dq(a, rope ? &t : nullptr, s)) != hipSuccess) return hip_fail(e, "backward dq");
   return S2ATTN_OK;
@@ -206,18 +209,20 @@ int do_bwd_stage(Stage stage, const void* q, const void* k, const void* v, const
   if (st) return st;
   if (B == 0 || N == 0) return S2ATTN_OK;
   const size_t qb = q_bytes(B, N, H, D), kb = q_bytes(B, N, Hkv, D), sb = stat_bytes(B, N, H);
-  const size_t need = round_up(sb);
+  const size_t need = 2 * round_up(sb);  // -Delta, then -lse*log2(e)
   if (ws_bytes < need) return fail(S2ATTN_EINVAL, "workspace too small");
   if (ws == nullptr || ((uintptr_t)ws & (kAlign - 1)) != 0)
     return fail(S2ATTN_EINVAL, "workspace is NULL or not 256-byte aligned");
   const hipStream_t s = (hipStream_t)stream;
+  float* ndelta = (float*)ws;
+  float* nlse2 = (float*)((char*)ws + round_up(sb));
   s2a::BwdArgs a{};
   a.q = (const uint16_t*)q;
   a.k = (const uint16_t*)k;
   a.v = (const uint16_t*)v;
   a.dout = (const uint16_t*)dout;
-  a.lse = lse;
-  a.delta = (const float*)ws;
+  a.nlse2 = nlse2;
+  a.ndelta = ndelta;
   a.dq = (uint16_t*)dq;
   a.dk = (uint16_t*)dk;
   a.dv = (uint16_t*)dv;
@@ -226,21 +231,19 @@ int do_bwd_stage(Stage stage, const void* q, const void* k, const void* v, const
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
   hipError_t e = hipSuccess;
   if (stage == Stage::kPre) {
-    Buf in[2] = {{out, qb, "out"}, {dout, qb, "dout"}};
+    Buf in[3] = {{out, qb, "out"}, {dout, qb, "dout"}, {lse, sb, "lse"}};
     Buf outs[1] = {{ws, need, "workspace"}};
-    if ((st = check_buffers(in, 2, outs, 1))) return st;
-    e = s2a::launch_bwd_delta((const uint16_t*)out, a.dout, (float*)ws, a.s, s);
+    if ((st = check_buffers(in, 3, outs, 1))) return st;
+    e = s2a::launch_bwd_delta((const uint16_t*)out, a.dout, lse, ndelta, nlse2, a.s, s);
   } else if (stage == Stage::kDkdv) {
-    Buf in[6] = {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"}, {lse, sb, "lse"}, {dout, qb, "dout"},
-                 {ws, need, "workspace"}};
+    Buf in[5] = {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"}, {dout, qb, "dout"}, {ws, need, "workspace"}};
     Buf outs[2] = {{dk, kb, "dk"}, {dv, kb, "dv"}};
-    if ((st = check_buffers(in, 6, outs, 2))) return st;
+    if ((st = check_buffers(in, 5, outs, 2))) return st;
     e = s2a::launch_bwd_dkdv(a, nullptr, s);
   } else {
-    Buf in[6] = {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"}, {lse, sb, "lse"}, {dout, qb, "dout"},
-                 {ws, need, "workspace"}};
+    Buf in[5] = {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"}, {dout, qb, "dout"}, {ws, need, "workspace"}};
     Buf outs[1] = {{dq, qb, "dq"}};
-    if ((st = check_buffers(in, 6, outs, 1))) return st;
+    if ((st = check_buffers(in, 5, outs, 1))) return st;
     e = s2a::launch_bwd_dq(a, nullptr, s);
   }
   if (e != hipSuccess) return hip_fail(e, "backward stage");
@@ -255,7 +258,7 @@ size_t fwd_rope_ws(int B, int N, int H, int Hkv, int D) {
 
 size_t bwd_ws(int B, int N, int H, int Hkv, int D, bool rope) {
   if (B <= 0 || N <= 0 || H <= 0 || Hkv <= 0 || D <= 0) return 0;
-  size_t n = round_up(stat_bytes(B, N, H));
+  size_t n = 2 * round_up(stat_bytes(B, N, H));
   if (rope) n += round_up(q_bytes(B, N, H, D)) + round_up(q_bytes(B, N, Hkv, D));
   return n;
 }
@@ -280,28 +283,27 @@ int s2attn_bwd(const void* q, const void* k, const void* v, const void* out, con
   });
 }
 
-int s2attn_bwd_preprocess(const void* out, const void* dout, int B, int N, int H, int D, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+int s2attn_bwd_preprocess(const void* out, const void* dout, const float* lse, int B, int N, int H, int D,
+                          void* workspace, size_t workspace_bytes, void* stream) {
   return guarded([&] {
-    return do_bwd_stage(Stage::kPre, nullptr, nullptr, nullptr, out, nullptr, dout, nullptr, nullptr, nullptr, B, N,
+    return do_bwd_stage(Stage::kPre, nullptr, nullptr, nullptr, out, lse, dout, nullptr, nullptr, nullptr, B, N,
                         H, H, D, 1, 0, workspace, workspace_bytes, stream);
   });
 }
 
-int s2attn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dout, void* dk,
-                    void* dv, int B, int N, int H, int Hkv, int D, int G, int shift, const void* workspace,
-                    size_t workspace_bytes, void* stream) {
+int s2attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, void* dk, void* dv, int B, int N,
+                    int H, int Hkv, int D, int G, int shift, const void* workspace, size_t workspace_bytes,
+                    void* stream) {
   return guarded([&] {
-    return do_bwd_stage(Stage::kDkdv, q, k, v, nullptr, lse, dout, nullptr, dk, dv, B, N, H, Hkv, D, G, shift,
+    return do_bwd_stage(Stage::kDkdv, q, k, v, nullptr, nullptr, dout, nullptr, dk, dv, B, N, H, Hkv, D, G, shift,
                         workspace, workspace_bytes, stream);
   });
 }
 
-int s2attn_bwd_dq(const void* q, const void* k, const void* v, const float* lse, const void* dout, void* dq, int B,
-                  int N, int H, int Hkv, int D, int G, int shift, const void* workspace, size_t workspace_bytes,
-                  void* stream) {
+int s2attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout, void* dq, int B, int N, int H,
+                  int Hkv, int D, int G, int shift, const void* workspace, size_t workspace_bytes, void* stream) {
   return guarded([&] {
-    return do_bwd_stage(Stage::kDq, q, k, v, nullptr, lse, dout, dq, nullptr, nullptr, B, N, H, Hkv, D, G, shift,
+    return do_bwd_stage(Stage::kDq, q, k, v, nullptr, nullptr, dout, dq, nullptr, nullptr, B, N, H, Hkv, D, G, shift,
                         workspace, workspace_bytes, stream);
   });
 }

@@ -5,7 +5,10 @@
 // opening definition), recomputing P from the saved log-sum-exp:
 //   P = exp(S - lse),  dV = P^T dO,  dP = dO V^T,
 //   dS = P * (dP - Delta),  dQ = c dS K,  dK = c dS^T Q,   c = 1/sqrt(D)
-// per group of rolled rows.  Rows and keys are addressed at their original
+// per group of rolled rows.  The S accumulators start at -lse*log2(e) and
+// take one operand pre-scaled by c*log2(e) (one bf16 rounding), and the dP
+// accumulators start at -Delta (both from the preprocess pass), so that
+// P = exp2(acc) and dS = P * acc.  Rows and keys are addressed at their original
 // positions (the roll by -shift and its inverse folded into indices), so dQ,
 // dK, dV land where the forward read q, k, v.
 //
@@ -113,15 +116,29 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const bool qvalid = qi < s.G;
   const int qpos = qvalid ? orig_pos(base, qi, s.N) : 0;
   const long long qoff = ((long long)(b * (long long)s.N + qpos) * s.H + h) * D;
+  // q scaled by c*log2(e) (as in the forward), so S comes out in log2 units.
   bf16x8 qf[D / 16], dof[D / 16];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
-    qf[kk] = as_bf16x8(qvalid ? ld16(a.q + qoff + kk * 16 + hh * 8) : zero_u4());
+    float x[8];
+    unpack8(qvalid ? ld16(a.q + qoff + kk * 16 + hh * 8) : zero_u4(), x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] *= a.scale_log2;
+    qf[kk] = as_bf16x8(pack8(x));
     dof[kk] = as_bf16x8(qvalid ? ld16(a.dout + qoff + kk * 16 + hh * 8) : zero_u4());
   }
   const long long stat_off = ((long long)b * s.H + h) * s.N + qpos;
-  const float lse2 = qvalid ? a.lse[stat_off] * kLog2e : 0.f;
-  const float dlt = qvalid ? a.delta[stat_off] : 0.f;
+  // Accumulator start values: every element of a lane belongs to its row.
+  f32x16 s_init, dp_init;
+  {
+    const float nl = qvalid ? a.nlse2[stat_off] : 0.f;
+    const float nd = qvalid ? a.ndelta[stat_off] : 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s_init[r] = nl;
+      dp_init[r] = nd;
+    }
+  }
 
   f32x16 dq[D / 32];
 #pragma unroll
@@ -161,7 +178,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // row-major K tile.
 #pragma unroll
     for (int kb = 0; kb < kBN / 32; ++kb) {
-      f32x16 sc = zero16(), dp = zero16();
+      f32x16 sc, dp;
       {
         bf16x8 kf[2], vf[2];
         kf[0] = sw.row(kt, kb * 32, 0);
@@ -172,19 +189,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             kf[(kk + 1) & 1] = sw.row(kt, kb * 32, kk + 1);
             vf[(kk + 1) & 1] = sw.row(vt, kb * 32, kk + 1);
           }
-          sc = mfma32x32x16(kf[kk & 1], qf[kk], sc);
-          dp = mfma32x32x16(vf[kk & 1], dof[kk], dp);
+          sc = mfma32x32x16(kf[kk & 1], qf[kk], kk == 0 ? s_init : sc);
+          dp = mfma32x32x16(vf[kk & 1], dof[kk], kk == 0 ? dp_init : dp);
         }
       }
       float ds[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float p = fast_exp2(sc[r] * a.scale_log2 - lse2);
+        float p = fast_exp2(sc[r]);
         if constexpr (MASK) {
           const int j = key0 + kb * 32 + acc_row(r, hh);
           if (j > qi) p = 0.f;
         }
-        ds[r] = p * (dp[r] - dlt);
+        ds[r] = p * dp[r];
       }
       bf16x8 dsb[2];
       dsb[0] = cvt8(f32x8{ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]});
@@ -310,11 +327,18 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
   const bool kvalid = kj < s.G;
   const int kpos = kvalid ? orig_pos(base, kj, s.N) : 0;
   const long long koff = ((long long)b * s.N + kpos) * kv_row + (long long)kvh * D;
+  // The P wave's K is scaled by c*log2(e), so its S comes out in log2 units.
   const uint16_t* kv_src = ds_wave ? a.v : a.k;
+  const float kv_scale = ds_wave ? 1.f : a.scale_log2;
   bf16x8 kvf[D / 16];
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk)
-    kvf[kk] = as_bf16x8(kvalid ? ld16(kv_src + koff + kk * 16 + hh * 8) : zero_u4());
+  for (int kk = 0; kk < D / 16; ++kk) {
+    float x[8];
+    unpack8(kvalid ? ld16(kv_src + koff + kk * 16 + hh * 8) : zero_u4(), x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] *= kv_scale;
+    kvf[kk] = as_bf16x8(pack8(x));
+  }
 
   f32x16 acc[D / 32];  // dV^T (P wave) or dK^T (dS wave)
 #pragma unroll
@@ -355,7 +379,7 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
     if (wave == 0) {
       const int i = min(i0 + rowperm32(l32), s.G - 1);  // slot m holds tile row rowperm32(m)
       const long long so = ((long long)b * s.H + h) * s.N + orig_pos(base, i, s.N);
-      dma4((hh ? a.delta : a.lse) + so, stats(c));
+      dma4((hh ? a.ndelta : a.nlse2) + so, stats(c));
     }
   };
 
@@ -366,16 +390,29 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
     return key_start + (step - hi * steps_per_head) * kBMQ;
   };
 
-  // P wave: S = Q K^T (lane column = key, elements = rows
-  // 8*(r/4) + 4*hh + r%4 of the step), P = exp2(S*c*log2e - lse*log2e),
-  // publish P, dV^T += dO^T P.
+  // Accumulator start values for a step: element r of the lane belongs to
+  // row slot 8*(r/4) + 4*hh + r%4, whose statistic sits at that slot.
+  auto row_stats = [&](const float* st) __attribute__((always_inline)) -> f32x16 {
+    f32x16 v;
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(&st[8 * r4 + 4 * hh]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * r4 + e] = x[e];
+    }
+    return v;
+  };
+
+  // P wave: S = Q K^T - lse (log2 units; lane column = key, elements = rows
+  // 8*(r/4) + 4*hh + r%4 of the step), P = exp2(S), publish P,
+  // dV^T += dO^T P.
   auto p_step = [&](int step, auto mask_tag, auto c) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const uint16_t* qt = qbuf(c);
     const uint16_t* ot = obuf(c);
     const float* st = stats(c);
     const int i0 = step_i0(step);
-    f32x16 sc = zero16();
+    f32x16 sc = row_stats(st);
     {
       bf16x8 qa[2];
       qa[0] = sw.row(qt, 0, 0);
@@ -387,18 +424,13 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
     }
     float p[16];
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int row0 = 8 * r4 + 4 * hh;
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&st[row0]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float pv = fast_exp2(sc[r4 * 4 + e] * a.scale_log2 - l4[e] * kLog2e);
-        if constexpr (MASK) {
-          const int row = i0 + acc_row(4 * r4 + e, hh);
-          if (kj > row || row >= s.G) pv = 0.f;
-        }
-        p[r4 * 4 + e] = pv;
+    for (int r = 0; r < 16; ++r) {
+      float pv = fast_exp2(sc[r]);
+      if constexpr (MASK) {
+        const int row = i0 + acc_row(r, hh);
+        if (kj > row || row >= s.G) pv = 0.f;
       }
+      p[r] = pv;
     }
     bf16x8 pb[2];
     pb[0] = cvt8(f32x8{p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]});
@@ -415,13 +447,13 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
     }
   };
 
-  // dS wave (one step behind): dP = dO V^T, dS = P (dP - Delta) with the P
+  // dS wave (one step behind): dP = dO V^T - Delta, dS = P dP with the P
   // wave's published P, dK^T += Q^T dS.
   auto ds_step = [&](int step, auto c) __attribute__((always_inline)) {
     const uint16_t* qt = qbuf(c);
     const uint16_t* ot = obuf(c);
     const float* st = stats(c);
-    f32x16 dp = zero16();
+    f32x16 dp = row_stats(st + kBMQ);
     {
       bf16x8 oa[2];
       oa[0] = sw.row(ot, 0, 0);
@@ -435,16 +467,7 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
     const bf16x8 pb1 = __builtin_bit_cast(bf16x8, Pbuf[step & 1][pair][1][lane]);
     float ds[16];
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int row0 = 8 * r4 + 4 * hh;
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&st[kBMQ + row0]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = r4 * 4 + e;
-        const float pv = (float)(r < 8 ? pb0[r] : pb1[r - 8]);
-        ds[r] = pv * (dp[r] - d4[e]);
-      }
-    }
+    for (int r = 0; r < 16; ++r) ds[r] = (float)(r < 8 ? pb0[r] : pb1[r - 8]) * dp[r];
     bf16x8 dsb[2];
     dsb[0] = cvt8(f32x8{ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]});
     dsb[1] = cvt8(f32x8{ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]});

@@ -36,8 +36,8 @@ struct BwdArgs {
   const uint16_t* k;     // [B, N, Hkv, D] (rotated copy when rope is on)
   const uint16_t* v;
   const uint16_t* dout;  // [B, N, H, D]
-  const float* lse;      // [B, H, N]
-  const float* delta;    // [B, H, N]: sum_d dout * out
+  const float* nlse2;    // [B, H, N]: -lse * log2(e)        (written by the preprocess pass)
+  const float* ndelta;   // [B, H, N]: -sum_d dout * out      (written by the preprocess pass)
   uint16_t* dq;          // [B, N, H, D]
   uint16_t* dk;          // [B, N, Hkv, D]
   uint16_t* dv;
@@ -49,8 +49,8 @@ struct BwdArgs {
 
 // Launchers: enqueue on `stream`, return the HIP status of the launch.
 hipError_t launch_fwd(const FwdArgs& a, const RopeTable* rope, hipStream_t stream);
-hipError_t launch_bwd_delta(const uint16_t* out, const uint16_t* dout, float* delta,
-                            const Shape& s, hipStream_t stream);
+hipError_t launch_bwd_delta(const uint16_t* out, const uint16_t* dout, const float* lse, float* ndelta,
+                            float* nlse2, const Shape& s, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, const RopeTable* rope, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, const RopeTable* rope, hipStream_t stream);
 // Rotate rows*heads*D bf16 values of a [B, N, heads, D] tensor into dst.

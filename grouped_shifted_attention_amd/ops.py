@@ -117,38 +117,37 @@ def s2attn_bwd(q, k, v, out, lse, dout, G, shift, dq=None, dk=None, dv=None, wor
     return dq, dk, dv
 
 
-def s2attn_bwd_preprocess(out, dout, workspace):
-    """Stage 1 of the backward: Delta into the workspace."""
+def s2attn_bwd_preprocess(out, dout, lse, workspace):
+    """Stage 1 of the backward: the row statistics (-Delta, -lse*log2 e) into the workspace."""
     B, N, H, D = out.shape
     _need(out, "out", torch.bfloat16, (B, N, H, D), None)
     _need(dout, "dout", torch.bfloat16, (B, N, H, D), out.device)
-    check(lib().s2attn_bwd_preprocess(_ptr(out), _ptr(dout), B, N, H, D, _ptr(workspace),
+    _need(lse, "lse", torch.float32, (B, H, N), out.device)
+    check(lib().s2attn_bwd_preprocess(_ptr(out), _ptr(dout), _ptr(lse), B, N, H, D, _ptr(workspace),
                                       workspace.numel() * workspace.element_size(), _stream(out)))
 
 
-def s2attn_bwd_dkdv(q, k, v, lse, dout, G, shift, workspace, dk=None, dv=None):
+def s2attn_bwd_dkdv(q, k, v, dout, G, shift, workspace, dk=None, dv=None):
     """Stage 2 of the backward: dk, dv (needs the preprocess stage's workspace)."""
     B, N, H, Hkv, D = _dims(q, k, v)
-    _need(lse, "lse", torch.float32, (B, H, N), q.device)
     _need(dout, "dout", torch.bfloat16, (B, N, H, D), q.device)
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     _need(dk, "dk", torch.bfloat16, (B, N, Hkv, D), q.device)
     _need(dv, "dv", torch.bfloat16, (B, N, Hkv, D), q.device)
-    check(lib().s2attn_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dout), _ptr(dk), _ptr(dv),
+    check(lib().s2attn_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dk), _ptr(dv),
                                 B, N, H, Hkv, D, int(G), int(shift), _ptr(workspace),
                                 workspace.numel() * workspace.element_size(), _stream(q)))
     return dk, dv
 
 
-def s2attn_bwd_dq(q, k, v, lse, dout, G, shift, workspace, dq=None):
+def s2attn_bwd_dq(q, k, v, dout, G, shift, workspace, dq=None):
     """Stage 3 of the backward: dq (needs the preprocess stage's workspace)."""
     B, N, H, Hkv, D = _dims(q, k, v)
-    _need(lse, "lse", torch.float32, (B, H, N), q.device)
     _need(dout, "dout", torch.bfloat16, (B, N, H, D), q.device)
     dq = torch.empty_like(q) if dq is None else dq
     _need(dq, "dq", torch.bfloat16, (B, N, H, D), q.device)
-    check(lib().s2attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dout), _ptr(dq),
+    check(lib().s2attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq),
                               B, N, H, Hkv, D, int(G), int(shift), _ptr(workspace),
                               workspace.numel() * workspace.element_size(), _stream(q)))
     return dq

@@ -63,8 +63,9 @@ int s2attn_fwd(const void* q, const void* k, const void* v, void* out, float* ls
                int B, int N, int H, int Hkv, int D, int G, int shift, void* stream);
 
 /*
- * Workspace bytes s2attn_bwd needs: the per-row dot products
- * Delta[b, h, n] = sum_d dout * out (float32, [B, H, N]).
+ * Workspace bytes s2attn_bwd needs: two float32 [B, H, N] row statistics,
+ * -Delta[b, h, n] = -sum_d dout * out and -lse[b, h, n] * log2(e), each
+ * starting on a 256-byte boundary.
  */
 size_t s2attn_bwd_workspace_size(int B, int N, int H, int Hkv, int D);
 
@@ -84,21 +85,23 @@ int s2attn_bwd(const void* q, const void* k, const void* v, const void* out, con
 /*
  * The backward in stages: the same kernels s2attn_bwd enqueues, in the same
  * order, for callers that want to schedule or time them separately.
- *   s2attn_bwd_preprocess  Delta[b,h,n] = sum_d dout*out into the workspace
- *   s2attn_bwd_dkdv        dk, dv (reads Delta)
- *   s2attn_bwd_dq          dq     (reads Delta)
+ *   s2attn_bwd_preprocess  the row statistics (-Delta, -lse*log2(e)) from
+ *                          out, dout and the forward's lse into the workspace
+ *   s2attn_bwd_dkdv        dk, dv (reads the statistics)
+ *   s2attn_bwd_dq          dq     (reads the statistics)
  * dkdv and dq do not depend on each other and may run on different streams
  * once preprocess has completed.  Arguments and the workspace are those of
- * s2attn_bwd (workspace of s2attn_bwd_workspace_size() bytes).
+ * s2attn_bwd (workspace of s2attn_bwd_workspace_size() bytes); dkdv and dq
+ * only read the workspace.
  */
-int s2attn_bwd_preprocess(const void* out, const void* dout, int B, int N, int H, int D,
+int s2attn_bwd_preprocess(const void* out, const void* dout, const float* lse,
+                          int B, int N, int H, int D,
                           void* workspace, size_t workspace_bytes, void* stream);
-int s2attn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
-                    const void* dout, void* dk, void* dv,
+int s2attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
+                    void* dk, void* dv,
                     int B, int N, int H, int Hkv, int D, int G, int shift,
                     const void* workspace, size_t workspace_bytes, void* stream);
-int s2attn_bwd_dq(const void* q, const void* k, const void* v, const float* lse,
-                  const void* dout, void* dq,
+int s2attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout, void* dq,
                   int B, int N, int H, int Hkv, int D, int G, int shift,
                   const void* workspace, size_t workspace_bytes, void* stream);
 
