@@ -264,6 +264,9 @@ constexpr int kDkdvWaves = 2 * kDkdvPairs;
 constexpr int kBNK = kDkdvPairs * 32;  // keys per workgroup
 constexpr int kBMQ = 32;               // q rows per step
 constexpr int kStages = 4;
+#ifndef S2A_DKDV_VSTAGE
+#define S2A_DKDV_VSTAGE 1  // q/dout tiles staged through VGPRs (1) or loaded straight into LDS (0)
+#endif
 
 template <int D, bool ROPE>
 __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void dkdv_kernel(
@@ -383,6 +386,50 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
     }
   };
 
+#if S2A_DKDV_VSTAGE
+  // Staging through VGPRs instead: thread tid owns 16-byte chunks tid,
+  // tid + 512, ... of the step's q tile followed by its dout tile (chunk =
+  // tile row * D/8 + column chunk); wave 0 also loads the rows' statistics
+  // (lanes 0-31 -lse*log2 e, lanes 32-63 -Delta, slot m holding tile row
+  // rowperm32(m)).  Loads are issued at the start of an iteration and
+  // written to LDS at its end.
+  constexpr int kCh = D / 8;
+  constexpr int kChunks = kBMQ * kCh;  // per tensor
+  constexpr int kThreads = kDkdvWaves * 64;
+  static_assert(2 * kChunks % kThreads == 0, "whole chunks per thread");
+  constexpr int kPer = 2 * kChunks / kThreads;
+  u32x4 stg[kPer];
+  float stg_stat = 0.f;
+  auto gload_step = [&](int step) __attribute__((always_inline)) {
+    const int hi = step / steps_per_head;
+    const int i0 = key_start + (step - hi * steps_per_head) * kBMQ;
+    const long long head_off = (long long)b * s.N * q_row + (long long)(h0 + hi) * D;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int item = tid + i * kThreads;
+      const int tensor = item / kChunks;
+      const int rem = item - tensor * kChunks;
+      const int row = min(i0 + rem / kCh, s.G - 1);
+      stg[i] = ld16((tensor ? a.dout : a.q) + head_off + orig_pos(base, row, s.N) * q_row + (rem % kCh) * 8);
+    }
+    if (wave == 0) {
+      const int i = min(i0 + rowperm32(l32), s.G - 1);
+      const long long so = ((long long)b * s.H + h0 + hi) * s.N + orig_pos(base, i, s.N);
+      stg_stat = (hh ? a.ndelta : a.nlse2)[so];
+    }
+  };
+  auto swrite_step = [&](auto c) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int item = tid + i * kThreads;
+      const int tensor = item / kChunks;
+      const int rem = item - tensor * kChunks;
+      st16((tensor ? obuf(c) : qbuf(c)) + (rem / kCh) * (D + 8) + (rem % kCh) * 8, stg[i]);
+    }
+    if (wave == 0) stats(c)[lane] = stg_stat;
+  };
+#endif
+
   // Row offset of a step inside its q head's block sequence, and whether a
   // step's rows can see any of this pair's keys / cross its diagonal.
   auto step_i0 = [&](int step) __attribute__((always_inline)) {
@@ -497,9 +544,21 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
   using S1 = std::integral_constant<int, 1>;
   using S2 = std::integral_constant<int, 2>;
   using S3 = std::integral_constant<int, 3>;
+#if S2A_DKDV_VSTAGE
+  (void)loads_per_step;
+  if (nsteps > 0) {
+    gload_step(0);
+    swrite_step(S0{});
+  }
+  if (nsteps > 1) {
+    gload_step(1);
+    swrite_step(S1{});
+  }
+#else
   if (nsteps > 0) load_step(0, S0{});
   if (nsteps > 1) load_step(1, S1{});
   wait_vmcnt_dyn(nsteps > 1 ? loads_per_step : 0);
+#endif
   lds_barrier();
 
   // Iteration n (stage c = n & 3): the P wave does step n, the dS wave step
@@ -507,7 +566,11 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
   // n-2.  nsteps+1 iterations in all, identical for every wave.
   auto iter = [&](int n, auto c) __attribute__((always_inline)) {
     constexpr int C = decltype(c)::value;
+#if S2A_DKDV_VSTAGE
+    if (n + 2 < nsteps) gload_step(n + 2);
+#else
     if (n + 2 < nsteps) load_step(n + 2, std::integral_constant<int, (C + 2) & 3>{});
+#endif
     if (!ds_wave) {
       if (n < nsteps) {
         const int kind = step_kind(n);
@@ -519,7 +582,11 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
     } else {
       if (n >= 1 && step_kind(n - 1) != 0) ds_step(n - 1, std::integral_constant<int, (C + 3) & 3>{});
     }
+#if S2A_DKDV_VSTAGE
+    if (n + 2 < nsteps) swrite_step(std::integral_constant<int, (C + 2) & 3>{});
+#else
     wait_vmcnt_dyn(n + 2 < nsteps ? loads_per_step : 0);
+#endif
     lds_barrier();
   };
   for (int n = 0; n <= nsteps; n += 4) {

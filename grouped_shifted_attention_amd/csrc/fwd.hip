@@ -29,33 +29,37 @@ namespace s2a {
 namespace {
 
 constexpr int kBN = 64;
+#ifndef S2A_FWD_VSTAGE
+#define S2A_FWD_VSTAGE 1  // eight-wave workgroups stage K/V through VGPRs (1) or load straight into LDS (0)
+#endif
 constexpr float kLazy = 8.f;  // log2-domain slack before the softmax reference moves
 
 template <int D, int NW, bool ROPE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_kernel(FwdArgs a, RopeTable rope) {
   constexpr int BM = NW * 32;
   using TileStage = LdsStage<D, kBN, NW>;
-  // K/V tile ring of NBUF stages (tile n in stage n % NBUF), each stage two
+  // Double-buffered K/V tiles (tile n in buffer n & 1), each buffer two
   // distinct LDS objects named at compile time: the compiler can then tell
-  // the reads of one stage from the direct loads filling another and does
-  // not make the reads wait for tiles still in flight.  Eight-wave
-  // workgroups (one per CU) afford three stages, so a tile's loads are
-  // issued two steps before it is read; four-wave ones (two per CU) two.
-  constexpr int NBUF = NW >= 8 ? 3 : 2;
+  // the reads of one buffer from the loads filling the other and does not
+  // make the reads wait for a tile still in flight.  Eight-wave workgroups
+  // stage K/V through VGPRs (VST): each thread loads its chunks of tile n+1
+  // at the start of step n and writes them to LDS at its end, which on
+  // gfx950 competes far less with the step's LDS reads than direct-to-LDS
+  // loads do.  Smaller workgroups load straight into LDS.
+  constexpr bool VST = NW >= 8 && S2A_FWD_VSTAGE;
   __shared__ __attribute__((aligned(16))) uint16_t Ks0[TileStage::ELEMS];
   __shared__ __attribute__((aligned(16))) uint16_t Ks1[TileStage::ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t Ks2[NBUF > 2 ? TileStage::ELEMS : 8];
   __shared__ __attribute__((aligned(16))) uint16_t Vs0[TileStage::ELEMS];
   __shared__ __attribute__((aligned(16))) uint16_t Vs1[TileStage::ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs2[NBUF > 2 ? TileStage::ELEMS : 8];
   auto kbuf = [&](auto c) __attribute__((always_inline)) -> uint16_t* {
-    constexpr int C = decltype(c)::value;
-    if constexpr (C == 0) return Ks0; else if constexpr (C == 1) return Ks1; else return Ks2;
+    if constexpr (decltype(c)::value) return Ks1; else return Ks0;
   };
   auto vbuf = [&](auto c) __attribute__((always_inline)) -> uint16_t* {
-    constexpr int C = decltype(c)::value;
-    if constexpr (C == 0) return Vs0; else if constexpr (C == 1) return Vs1; else return Vs2;
+    if constexpr (decltype(c)::value) return Vs1; else return Vs0;
   };
+  using P0 = std::false_type;
+  using P1 = std::true_type;
+
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep it scalar
   const int lane = tid & 63;
@@ -140,8 +144,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // above them, which the mask zeroes) do.
   const int n_full = min(ntiles, (wave_q0 + 1) / kBN);
 
-  // One k/v tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
-  auto compute = [&](int n, auto c) __attribute__((always_inline)) {
+  // One k/v tile: S^T = K Q^T, online softmax, O^T += V^T P^T.  MASK only
+  // for the tiles from n_full on.
+  auto compute = [&](int n, auto mask_tag, auto c) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int key0 = n * kBN;
     // S^T: the two 32-key blocks are independent accumulators, interleaved
     // so back-to-back MFMAs never wait on each other; K fragments are read
@@ -178,7 +184,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         if (i < (D / 16 - (KD - 1)) * NB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
     }
-    if (n >= n_full) {
+    if constexpr (MASK) {
 #pragma unroll
       for (int kb = 0; kb < kBN / 32; ++kb)
 #pragma unroll
@@ -258,34 +264,83 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
   };
 
-  // Step n (stage C = n % NBUF): start loading tile n + NBUF - 1 into the
-  // stage step n - 1 finished with, compute tile n, wait for tile n + 1
-  // (later tiles' loads stay in flight) and meet at the barrier.  Every wave
-  // runs ntiles steps, so the barriers match.
-  const int loads_per_tile = 2 * TileStage::count(wave);
-  auto step = [&](int n, auto c) __attribute__((always_inline)) {
-    constexpr int C = decltype(c)::value;
-    if (n + NBUF - 1 < ntiles) load_tile(n + NBUF - 1, std::integral_constant<int, (C + NBUF - 1) % NBUF>{});
-    compute(n, c);
-    wait_vmcnt_dyn(loads_per_tile * (min(n + NBUF - 1, ntiles - 1) - (n + 1)));
-    lds_barrier();
+  // VGPR staging (VST): thread tid owns 16-byte chunks tid, tid + NW*64, ...
+  // of the K tile followed by the V tile (chunk = tile row * D/8 + column
+  // chunk).  A contiguous tile needs one 64-bit add per chunk.
+  constexpr int kCh = D / 8;
+  constexpr int kThreads = NW * 64;
+  constexpr int kPer = VST ? 2 * kBN * kCh / kThreads : 1;
+  static_assert(!VST || (2 * kBN * kCh) % kThreads == 0, "whole chunks per thread");
+  u32x4 stg[kPer];
+  auto chunk = [&](int i, int& tensor, int& row, int& col) __attribute__((always_inline)) {
+    const int item = tid + i * kThreads;
+    tensor = item / (kBN * kCh);
+    const int rem = item - tensor * (kBN * kCh);
+    row = rem / kCh;
+    col = (rem % kCh) * 8;
+  };
+  auto gload_tile = [&](int n) __attribute__((always_inline)) {
+    const int key0 = n * kBN;
+    const uint16_t* kt = contig_tile(kb_ptr, kv_row, base, key0, kBN, s.G, s.N);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      int tensor, row, col;
+      chunk(i, tensor, row, col);
+      const uint16_t* head0 = tensor ? vb_ptr : kb_ptr;
+      const uint16_t* src;
+      if (kt != nullptr)
+        src = head0 + (kt - kb_ptr) + row * kv_row + col;
+      else
+        src = head0 + orig_pos(base, min(key0 + row, s.G - 1), s.N) * kv_row + col;
+      stg[i] = ld16(src);
+    }
+  };
+  auto swrite_tile = [&](auto c) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      int tensor, row, col;
+      chunk(i, tensor, row, col);
+      st16((tensor ? vbuf(c) : kbuf(c)) + row * (D + 8) + col, stg[i]);
+    }
   };
 
-#pragma unroll
-  for (int i = 0; i < NBUF - 1; ++i) {
-    if (i == 0) load_tile(0, std::integral_constant<int, 0>{});
-    if (i == 1 && ntiles > 1) load_tile(1, std::integral_constant<int, 1>{});
-  }
-  wait_vmcnt_dyn(loads_per_tile * (min(NBUF - 2, ntiles - 1)));
-  lds_barrier();
-
-  for (int n = 0; n < ntiles; n += NBUF) {
-    step(n, std::integral_constant<int, 0>{});
-    if (n + 1 < ntiles) step(n + 1, std::integral_constant<int, 1>{});
-    if constexpr (NBUF > 2) {
-      if (n + 2 < ntiles) step(n + 2, std::integral_constant<int, 2>{});
+  // Step n (buffer n & 1): start loading tile n+1 (into the other buffer,
+  // or into VGPRs written to it at the end), compute tile n, wait for tile
+  // n+1 and meet at the barrier.  Every wave runs ntiles steps, so the
+  // barriers match.
+  auto step = [&](int n, auto mask_tag, auto c) __attribute__((always_inline)) {
+    using Next = std::integral_constant<bool, !decltype(c)::value>;
+    if constexpr (VST) {
+      if (n + 1 < ntiles) gload_tile(n + 1);
+      compute(n, mask_tag, c);
+      if (n + 1 < ntiles) swrite_tile(Next{});
+    } else {
+      if (n + 1 < ntiles) load_tile(n + 1, Next{});
+      compute(n, mask_tag, c);
+      wait_vmem_all();
     }
+    lds_barrier();
+  };
+  // Steps n .. n1-1, unrolled by two so each names its buffer statically.
+  auto run = [&](int n, int n1, auto mask_tag) __attribute__((always_inline)) {
+    if (n < n1 && (n & 1)) step(n++, mask_tag, P1{});
+    for (; n + 1 < n1; n += 2) {
+      step(n, mask_tag, P0{});
+      step(n + 1, mask_tag, P1{});
+    }
+    if (n < n1) step(n, mask_tag, P0{});
+  };
+
+  if constexpr (VST) {
+    gload_tile(0);
+    swrite_tile(P0{});
+  } else {
+    load_tile(0, P0{});
+    wait_vmem_all();
   }
+  lds_barrier();
+  run(0, n_full, std::false_type{});
+  run(n_full, ntiles, std::true_type{});
 
   // ---- epilogue: normalise, write O and LSE at the original position ----
   const float lt = half_sum(l_run);
@@ -306,7 +361,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 }
 
 #ifndef S2A_FWD_WAVES_LARGE
-#define S2A_FWD_WAVES_LARGE 4  // waves per workgroup for groups longer than 1024
+#define S2A_FWD_WAVES_LARGE 8  // waves per workgroup for groups longer than 1024
 #endif
 
 template <int D, int NW, bool ROPE>
