@@ -391,16 +391,18 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
   // tid + 512, ... of the step's q tile followed by its dout tile (chunk =
   // tile row * D/8 + column chunk); wave 0 also loads the rows' statistics
   // (lanes 0-31 -lse*log2 e, lanes 32-63 -Delta, slot m holding tile row
-  // rowperm32(m)).  Loads are issued at the start of an iteration and
-  // written to LDS at its end.
+  // rowperm32(m)).  Two register sets (step m in set m & 1): the loads of
+  // step n+3 are issued at the start of iteration n and written to LDS at
+  // the end of iteration n+1, so they have two iterations to arrive.
   constexpr int kCh = D / 8;
   constexpr int kChunks = kBMQ * kCh;  // per tensor
   constexpr int kThreads = kDkdvWaves * 64;
   static_assert(2 * kChunks % kThreads == 0, "whole chunks per thread");
   constexpr int kPer = 2 * kChunks / kThreads;
-  u32x4 stg[kPer];
-  float stg_stat = 0.f;
-  auto gload_step = [&](int step) __attribute__((always_inline)) {
+  u32x4 stg[2][kPer];
+  float stg_stat[2] = {0.f, 0.f};
+  auto gload_step = [&](int step, auto set) __attribute__((always_inline)) {
+    constexpr int R = decltype(set)::value;
     const int hi = step / steps_per_head;
     const int i0 = key_start + (step - hi * steps_per_head) * kBMQ;
     const long long head_off = (long long)b * s.N * q_row + (long long)(h0 + hi) * D;
@@ -410,23 +412,24 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
       const int tensor = item / kChunks;
       const int rem = item - tensor * kChunks;
       const int row = min(i0 + rem / kCh, s.G - 1);
-      stg[i] = ld16((tensor ? a.dout : a.q) + head_off + orig_pos(base, row, s.N) * q_row + (rem % kCh) * 8);
+      stg[R][i] = ld16((tensor ? a.dout : a.q) + head_off + orig_pos(base, row, s.N) * q_row + (rem % kCh) * 8);
     }
     if (wave == 0) {
       const int i = min(i0 + rowperm32(l32), s.G - 1);
       const long long so = ((long long)b * s.H + h0 + hi) * s.N + orig_pos(base, i, s.N);
-      stg_stat = (hh ? a.ndelta : a.nlse2)[so];
+      stg_stat[R] = (hh ? a.ndelta : a.nlse2)[so];
     }
   };
-  auto swrite_step = [&](auto c) __attribute__((always_inline)) {
+  auto swrite_step = [&](auto c, auto set) __attribute__((always_inline)) {
+    constexpr int R = decltype(set)::value;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int item = tid + i * kThreads;
       const int tensor = item / kChunks;
       const int rem = item - tensor * kChunks;
-      st16((tensor ? obuf(c) : qbuf(c)) + (rem / kCh) * (D + 8) + (rem % kCh) * 8, stg[i]);
+      st16((tensor ? obuf(c) : qbuf(c)) + (rem / kCh) * (D + 8) + (rem % kCh) * 8, stg[R][i]);
     }
-    if (wave == 0) stats(c)[lane] = stg_stat;
+    if (wave == 0) stats(c)[lane] = stg_stat[R];
   };
 #endif
 
@@ -546,14 +549,17 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
   using S3 = std::integral_constant<int, 3>;
 #if S2A_DKDV_VSTAGE
   (void)loads_per_step;
+  using R0 = std::integral_constant<int, 0>;
+  using R1 = std::integral_constant<int, 1>;
   if (nsteps > 0) {
-    gload_step(0);
-    swrite_step(S0{});
+    gload_step(0, R0{});
+    swrite_step(S0{}, R0{});
   }
   if (nsteps > 1) {
-    gload_step(1);
-    swrite_step(S1{});
+    gload_step(1, R1{});
+    swrite_step(S1{}, R1{});
   }
+  if (nsteps > 2) gload_step(2, R0{});
 #else
   if (nsteps > 0) load_step(0, S0{});
   if (nsteps > 1) load_step(1, S1{});
@@ -567,7 +573,7 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
   auto iter = [&](int n, auto c) __attribute__((always_inline)) {
     constexpr int C = decltype(c)::value;
 #if S2A_DKDV_VSTAGE
-    if (n + 2 < nsteps) gload_step(n + 2);
+    if (n + 3 < nsteps) gload_step(n + 3, std::integral_constant<int, (C + 1) & 1>{});
 #else
     if (n + 2 < nsteps) load_step(n + 2, std::integral_constant<int, (C + 2) & 3>{});
 #endif
@@ -583,7 +589,7 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
       if (n >= 1 && step_kind(n - 1) != 0) ds_step(n - 1, std::integral_constant<int, (C + 3) & 3>{});
     }
 #if S2A_DKDV_VSTAGE
-    if (n + 2 < nsteps) swrite_step(std::integral_constant<int, (C + 2) & 3>{});
+    if (n + 2 < nsteps) swrite_step(std::integral_constant<int, (C + 2) & 3>{}, std::integral_constant<int, C & 1>{});
 #else
     wait_vmcnt_dyn(n + 2 < nsteps ? loads_per_step : 0);
 #endif
