@@ -53,6 +53,8 @@ int check_shape(int B, int N, int H, int Hkv, int D, int G, int shift) {
   // Element counts in 64-bit; workgroup counts must fit a 1-D grid.
   const double elems = (double)B * N * H * D;
   if (elems > 4.0e18) return fail(S2ATTN_EINVAL, "tensor too large");
+  // Kernels address a tile of 64 consecutive rows with 32-bit offsets.
+  if (64.0 * H * D >= 2147483648.0) return fail(S2ATTN_EINVAL, "H * D too large");
   const double wgs = (double)B * H * ((double)N / G) * ((G + 31) / 32);
   if (wgs > 2147483647.0) return fail(S2ATTN_EINVAL, "too many work items for one launch");
   return S2ATTN_OK;

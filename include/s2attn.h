@@ -38,7 +38,9 @@
  * Accepted shapes: B >= 0, N >= 0, H >= 1, 1 <= Hkv, H % Hkv == 0, G >= 1,
  * N % G == 0, 0 <= shift < G; with shift > 0, H and Hkv must be even (so the
  * shifted q heads read exactly the shifted k/v heads).  D must be 64 or 128
- * (else S2ATTN_EUNSUPPORTED).  B == 0 or N == 0 is a valid empty call.
+ * (else S2ATTN_EUNSUPPORTED).  64 * H * D must stay below 2^31 (the kernels
+ * address 64-row tiles with 32-bit offsets).  B == 0 or N == 0 is a valid
+ * empty call.
  */
 #ifndef S2ATTN_H
 #define S2ATTN_H

@@ -82,6 +82,7 @@ def detail():
     (dict(B=-1), ">= 0"),
     (dict(H=0), ">= 1"),
     (dict(D=0), "D must be"),
+    (dict(H=262144, Hkv=262144, D=128, shift=0), "H * D too large"),
 ])
 def test_fwd_rejects_bad_shapes(kw, msg):
     assert fwd(**kw) == EINVAL
