@@ -401,10 +401,18 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
   constexpr int kPer = 2 * kChunks / kThreads;
   u32x4 stg[2][kPer];
   float stg_stat[2] = {0.f, 0.f};
-  auto gload_step = [&](int step, auto set) __attribute__((always_inline)) {
+  // Steps are loaded in order; (ld_hi, ld_i0) is the q head and first row of
+  // the next one (a running count, no division per step).
+  int ld_hi = 0, ld_i0 = key_start;
+  const int row_stop = key_start + steps_per_head * kBMQ;
+  auto gload_step = [&](auto set) __attribute__((always_inline)) {
     constexpr int R = decltype(set)::value;
-    const int hi = step / steps_per_head;
-    const int i0 = key_start + (step - hi * steps_per_head) * kBMQ;
+    const int hi = ld_hi, i0 = ld_i0;
+    ld_i0 += kBMQ;
+    if (ld_i0 == row_stop) {
+      ld_i0 = key_start;
+      ++ld_hi;
+    }
     const long long head_off = (long long)b * s.N * q_row + (long long)(h0 + hi) * D;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
@@ -433,13 +441,6 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
   };
 #endif
 
-  // Row offset of a step inside its q head's block sequence, and whether a
-  // step's rows can see any of this pair's keys / cross its diagonal.
-  auto step_i0 = [&](int step) __attribute__((always_inline)) {
-    const int hi = step / steps_per_head;
-    return key_start + (step - hi * steps_per_head) * kBMQ;
-  };
-
   // Accumulator start values for a step: element r of the lane belongs to
   // row slot 8*(r/4) + 4*hh + r%4, whose statistic sits at that slot.
   auto row_stats = [&](const float* st) __attribute__((always_inline)) -> f32x16 {
@@ -456,12 +457,11 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
   // P wave: S = Q K^T - lse (log2 units; lane column = key, elements = rows
   // 8*(r/4) + 4*hh + r%4 of the step), P = exp2(S), publish P,
   // dV^T += dO^T P.
-  auto p_step = [&](int step, auto mask_tag, auto c) __attribute__((always_inline)) {
+  auto p_step = [&](int step, int i0, auto mask_tag, auto c) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const uint16_t* qt = qbuf(c);
     const uint16_t* ot = obuf(c);
     const float* st = stats(c);
-    const int i0 = step_i0(step);
     f32x16 sc = row_stats(st);
     {
       bf16x8 qa[2];
@@ -537,10 +537,11 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
   const int skip = min(steps_per_head, (kw0 - key_start) / kBMQ);
   const int diag_end = min(steps_per_head, (kw0 + 31 - key_start) / kBMQ + 1);
   const int ragged = ((s.G - key_start) % kBMQ) != 0 ? steps_per_head - 1 : steps_per_head;
-  auto step_kind = [&](int step) __attribute__((always_inline)) {  // 0 skip, 1 masked, 2 full
-    const int j = step % steps_per_head;
+  // j: a step's index inside its q head's block sequence.
+  auto step_kind = [&](int j) __attribute__((always_inline)) {  // 0 skip, 1 masked, 2 full
     return j < skip ? 0 : ((j < diag_end || j >= ragged) ? 1 : 2);
   };
+  int cur_j = 0, prev_j = 0;  // j of step n (P wave) and of step n-1 (dS wave)
 
   const int loads_per_step = 2 * TileStage::count(wave) + (wave == 0 ? 1 : 0);
   using S0 = std::integral_constant<int, 0>;
@@ -552,14 +553,14 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
   using R0 = std::integral_constant<int, 0>;
   using R1 = std::integral_constant<int, 1>;
   if (nsteps > 0) {
-    gload_step(0, R0{});
+    gload_step(R0{});
     swrite_step(S0{}, R0{});
   }
   if (nsteps > 1) {
-    gload_step(1, R1{});
+    gload_step(R1{});
     swrite_step(S1{}, R1{});
   }
-  if (nsteps > 2) gload_step(2, R0{});
+  if (nsteps > 2) gload_step(R0{});
 #else
   if (nsteps > 0) load_step(0, S0{});
   if (nsteps > 1) load_step(1, S1{});
@@ -573,21 +574,24 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
   auto iter = [&](int n, auto c) __attribute__((always_inline)) {
     constexpr int C = decltype(c)::value;
 #if S2A_DKDV_VSTAGE
-    if (n + 3 < nsteps) gload_step(n + 3, std::integral_constant<int, (C + 1) & 1>{});
+    if (n + 3 < nsteps) gload_step(std::integral_constant<int, (C + 1) & 1>{});
 #else
     if (n + 2 < nsteps) load_step(n + 2, std::integral_constant<int, (C + 2) & 3>{});
 #endif
     if (!ds_wave) {
       if (n < nsteps) {
-        const int kind = step_kind(n);
+        const int kind = step_kind(cur_j);
+        const int i0 = key_start + cur_j * kBMQ;
         if (kind == 2)
-          p_step(n, std::false_type{}, c);
+          p_step(n, i0, std::false_type{}, c);
         else if (kind == 1)
-          p_step(n, std::true_type{}, c);
+          p_step(n, i0, std::true_type{}, c);
       }
     } else {
-      if (n >= 1 && step_kind(n - 1) != 0) ds_step(n - 1, std::integral_constant<int, (C + 3) & 3>{});
+      if (n >= 1 && step_kind(prev_j) != 0) ds_step(n - 1, std::integral_constant<int, (C + 3) & 3>{});
     }
+    prev_j = cur_j;
+    cur_j = cur_j + 1 == steps_per_head ? 0 : cur_j + 1;
 #if S2A_DKDV_VSTAGE
     if (n + 2 < nsteps) swrite_step(std::integral_constant<int, (C + 2) & 3>{}, std::integral_constant<int, C & 1>{});
 #else
