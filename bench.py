@@ -17,7 +17,8 @@ Prints ONE JSON line.  Options:
   --gpus N        only 1 is supported (the path is single-GPU)
   --steps K       timed steps (default 20)
   --warmup W      untimed steps first (default 5)
-  --workload W    a key of workloads.WORKLOADS without RoPE
+  --workload W    a key of workloads.WORKLOADS (with RoPE: the fused entry
+                  points are timed as two units, forward and backward)
   --no-cpu-baseline   skip timing the fp64 oracle on a sample
   --calib-copy-mib M  also run one plain device copy of M MiB (for counter calibration)
 """
@@ -70,8 +71,8 @@ def cpu_baseline(cfg, x_bits, budget_s=20.0):
         f64 = lambda name, hh: workloads.f64_from_bf16_bits(x_bits[name][0, :, hh, :])
         qh, kh, vh, doh = f64("q", h), f64("k", kvh), f64("v", kvh), f64("dout", h)
         shh = oracle.head_shift(h, H, sh)
-        oracle.head_unit_forward(qh, kh, vh, G, shh, g)
-        oracle.head_unit_backward(qh, kh, vh, doh, G, shh, g)
+        oracle.head_unit_forward(qh, kh, vh, G, shh, g, rope=cfg["rope"])
+        oracle.head_unit_backward(qh, kh, vh, doh, G, shh, g, rope=cfg["rope"])
         done += 1
         if time.perf_counter() - t0 > budget_s:
             break
@@ -117,8 +118,7 @@ def main():
 
     name = args.workload or workloads.BENCH_WORKLOAD
     cfg = dict(workloads.WORKLOADS[name], name=name)
-    if cfg["rope"] is not None:
-        raise SystemExit("bench.py times the workloads without RoPE")
+    rope = cfg["rope"]
     B, N, H, Hkv, D, G, sh = (cfg[k] for k in ("B", "N", "H", "Hkv", "D", "G", "shift"))
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
@@ -131,7 +131,8 @@ def main():
     out = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = ops.bwd_workspace(q, k)
+    ws = ops.bwd_workspace(q, k, rope=rope is not None)
+    ws_f = ops.fwd_rope_workspace(q, k) if rope is not None else None
     stream = torch.cuda.current_stream(dev)
 
     if args.calib_copy_mib > 0:
@@ -143,27 +144,44 @@ def main():
         del src, dst
 
     kernels = ["fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq"]
+    if rope is not None:
+        # The fused RoPE entry points have no stage calls: time the forward
+        # (k rotation + attention) and the backward (q, k rotations, the
+        # statistics pass, dK/dV, dQ) as whole calls.
+        kernels = ["fwd_rope", "bwd_rope"]
+
+    def step_rope(events=None):
+        if events is not None:
+            events[0].record(stream)
+        ops.s2attn_fwd_rope(q, k, v, G, sh, *rope, out=out, lse=lse, workspace=ws_f)
+        if events is not None:
+            events[1].record(stream)
+        ops.s2attn_bwd_rope(q, k, v, out, lse, do, G, sh, *rope, dq=dq, dk=dk, dv=dv, workspace=ws)
+        if events is not None:
+            events[2].record(stream)
 
     def step(events=None):
+        if rope is not None:
+            return step_rope(events)
         if events is not None:
             events[0].record(stream)
         ops.s2attn_fwd(q, k, v, G, sh, out=out, lse=lse)
         if events is not None:
             events[1].record(stream)
-        ops.s2attn_bwd_preprocess(out, do, lse, ws)
+        ops.s2attn_bwd_preprocess(q, out, do, lse, ws)
         if events is not None:
             events[2].record(stream)
-        ops.s2attn_bwd_dkdv(q, k, v, do, G, sh, ws, dk=dk, dv=dv)
+        ops.s2attn_bwd_dkdv(k, v, do, G, sh, ws, dk=dk, dv=dv)
         if events is not None:
             events[3].record(stream)
-        ops.s2attn_bwd_dq(q, k, v, do, G, sh, ws, dq=dq)
+        ops.s2attn_bwd_dq(k, v, do, G, sh, ws, dq=dq)
         if events is not None:
             events[4].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -182,6 +200,8 @@ def main():
     # forward 2 products, dK/dV 4 (S, dP, dV, dK), dQ 3 (S, dP, dQ).
     unit = B * H * N * G * D
     kernel_flops = {"fwd": 2 * unit, "bwd_dkdv": 4 * unit, "bwd_dq": 3 * unit}
+    if rope is not None:
+        kernel_flops = {"fwd_rope": 2 * unit, "bwd_rope": 7 * unit}
     dominant = max(kernel_flops, key=lambda kname: kernel_ms[kname])
     achieved = kernel_flops[dominant] / (kernel_ms[dominant] * 1e-3) / 1e12
     roofline = {
@@ -211,14 +231,14 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": name, "B": B, "N": N, "H": H, "Hkv": Hkv, "D": D, "G": G, "shift": sh,
-                   "parallelism": "single-gpu"},
+                   "rope": list(rope) if rope is not None else None, "parallelism": "single-gpu"},
         "pct_peak": 100.0 * value / PEAK_BF16_TFLOPS,
-        "fwd_tflops": f_fwd / (kernel_ms["fwd"] * 1e-3) / 1e12,
+        "fwd_tflops": f_fwd / (kernel_ms[kernels[0]] * 1e-3) / 1e12,
         "bwd_tflops": f_bwd / (sum(kernel_ms[kk] for kk in kernels[1:]) * 1e-3) / 1e12,
         "kernel_ms": kernel_ms,
         "roofline": roofline,
         "hbm_gbs_algorithmic": {
-            "fwd": flops.fwd_algorithmic_bytes(B, N, H, Hkv, D) / (kernel_ms["fwd"] * 1e-3) / 1e9,
+            "fwd": flops.fwd_algorithmic_bytes(B, N, H, Hkv, D) / (kernel_ms[kernels[0]] * 1e-3) / 1e9,
             "bwd": flops.bwd_algorithmic_bytes(B, N, H, Hkv, D)
             / (sum(kernel_ms[kk] for kk in kernels[1:]) * 1e-3) / 1e9,
             "peak": PEAK_HBM_GBS,

@@ -140,7 +140,7 @@ int do_fwd(const void* q, const void* k, const void* v, void* out, float* lse, i
   if (rope) {
     const s2a::RopeTable t = make_rope(D, rope[0], rope[1]);
     uint16_t* krot = (uint16_t*)ws;
-    if ((e = s2a::launch_rope_rotate(a.k, krot, a.s, Hkv, t, s)) != hipSuccess) return hip_fail(e, "rope(k)");
+    if ((e = s2a::launch_rope_rotate(a.k, krot, a.s, Hkv, t, 1.f, s)) != hipSuccess) return hip_fail(e, "rope(k)");
     a.k = krot;
     if ((e = s2a::launch_fwd(a, &t, s)) != hipSuccess) return hip_fail(e, "forward");
   } else {
@@ -158,7 +158,8 @@ int do_bwd(const void* q, const void* k, const void* v, const void* out, const f
   if (B == 0 || N == 0) return S2ATTN_OK;
   const size_t qb = q_bytes(B, N, H, D), kb = q_bytes(B, N, Hkv, D), sb = stat_bytes(B, N, H);
   const size_t stats = 2 * round_up(sb);  // -Delta, then -lse*log2(e)
-  const size_t need = rope ? stats + round_up(qb) + round_up(kb) : stats;
+  // then the scaled (and rotated) q copy, then the rotated k copy
+  const size_t need = stats + round_up(qb) + (rope ? round_up(kb) : 0);
   Buf in[6] = {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"}, {out, qb, "out"}, {lse, sb, "lse"}, {dout, qb, "dout"}};
   Buf outs[4] = {{dq, qb, "dq"}, {dk, kb, "dk"}, {dv, kb, "dv"}, {ws, need, "workspace"}};
   st = check_buffers(in, 6, outs, 4);
@@ -184,18 +185,19 @@ int do_bwd(const void* q, const void* k, const void* v, const void* out, const f
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
   hipError_t e;
   s2a::RopeTable t{};
+  uint16_t* qs = (uint16_t*)(w + stats);
   if (rope) {
     t = make_rope(D, rope[0], rope[1]);
-    uint16_t* qrot = (uint16_t*)(w + stats);
     uint16_t* krot = (uint16_t*)(w + stats + round_up(qb));
-    if ((e = s2a::launch_rope_rotate(a.q, qrot, a.s, H, t, s)) != hipSuccess) return hip_fail(e, "rope(q)");
-    if ((e = s2a::launch_rope_rotate(a.k, krot, a.s, Hkv, t, s)) != hipSuccess) return hip_fail(e, "rope(k)");
-    a.q = qrot;
+    if ((e = s2a::launch_rope_rotate(a.q, qs, a.s, H, t, a.scale_log2, s)) != hipSuccess)
+      return hip_fail(e, "rope(q)");
+    if ((e = s2a::launch_rope_rotate(a.k, krot, a.s, Hkv, t, 1.f, s)) != hipSuccess) return hip_fail(e, "rope(k)");
     a.k = krot;
   }
-  if ((e = s2a::launch_bwd_delta((const uint16_t*)out, (const uint16_t*)dout, lse, ndelta, nlse2, a.s, s)) !=
-      hipSuccess)
+  if ((e = s2a::launch_bwd_delta((const uint16_t*)out, (const uint16_t*)dout, lse, ndelta, nlse2,
+                                 rope ? nullptr : (const uint16_t*)q, qs, a.scale_log2, a.s, s)) != hipSuccess)
     return hip_fail(e, "backward preprocess");
+  a.q = qs;
   if ((e = s2a::launch_bwd_dkdv(a, rope ? &t : nullptr, s)) != hipSuccess) return hip_fail(e, "backward dk/dv");
   if ((e = s2a::launch_bwd_dq(a, rope ? &t : nullptr, s)) != hipSuccess) return hip_fail(e, "backward dq");
   return S2ATTN_OK;
@@ -211,15 +213,16 @@ int do_bwd_stage(Stage stage, const void* q, const void* k, const void* v, const
   if (st) return st;
   if (B == 0 || N == 0) return S2ATTN_OK;
   const size_t qb = q_bytes(B, N, H, D), kb = q_bytes(B, N, Hkv, D), sb = stat_bytes(B, N, H);
-  const size_t need = 2 * round_up(sb);  // -Delta, then -lse*log2(e)
+  const size_t need = 2 * round_up(sb) + round_up(qb);  // -Delta, -lse*log2(e), q*c*log2(e)
   if (ws_bytes < need) return fail(S2ATTN_EINVAL, "workspace too small");
   if (ws == nullptr || ((uintptr_t)ws & (kAlign - 1)) != 0)
     return fail(S2ATTN_EINVAL, "workspace is NULL or not 256-byte aligned");
   const hipStream_t s = (hipStream_t)stream;
   float* ndelta = (float*)ws;
   float* nlse2 = (float*)((char*)ws + round_up(sb));
+  uint16_t* qs = (uint16_t*)((char*)ws + 2 * round_up(sb));
   s2a::BwdArgs a{};
-  a.q = (const uint16_t*)q;
+  a.q = qs;
   a.k = (const uint16_t*)k;
   a.v = (const uint16_t*)v;
   a.dout = (const uint16_t*)dout;
@@ -233,19 +236,20 @@ int do_bwd_stage(Stage stage, const void* q, const void* k, const void* v, const
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
   hipError_t e = hipSuccess;
   if (stage == Stage::kPre) {
-    Buf in[3] = {{out, qb, "out"}, {dout, qb, "dout"}, {lse, sb, "lse"}};
+    Buf in[4] = {{q, qb, "q"}, {out, qb, "out"}, {dout, qb, "dout"}, {lse, sb, "lse"}};
     Buf outs[1] = {{ws, need, "workspace"}};
-    if ((st = check_buffers(in, 3, outs, 1))) return st;
-    e = s2a::launch_bwd_delta((const uint16_t*)out, a.dout, lse, ndelta, nlse2, a.s, s);
+    if ((st = check_buffers(in, 4, outs, 1))) return st;
+    e = s2a::launch_bwd_delta((const uint16_t*)out, a.dout, lse, ndelta, nlse2, (const uint16_t*)q, qs,
+                              a.scale_log2, a.s, s);
   } else if (stage == Stage::kDkdv) {
-    Buf in[5] = {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"}, {dout, qb, "dout"}, {ws, need, "workspace"}};
+    Buf in[4] = {{k, kb, "k"}, {v, kb, "v"}, {dout, qb, "dout"}, {ws, need, "workspace"}};
     Buf outs[2] = {{dk, kb, "dk"}, {dv, kb, "dv"}};
-    if ((st = check_buffers(in, 5, outs, 2))) return st;
+    if ((st = check_buffers(in, 4, outs, 2))) return st;
     e = s2a::launch_bwd_dkdv(a, nullptr, s);
   } else {
-    Buf in[5] = {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"}, {dout, qb, "dout"}, {ws, need, "workspace"}};
+    Buf in[4] = {{k, kb, "k"}, {v, kb, "v"}, {dout, qb, "dout"}, {ws, need, "workspace"}};
     Buf outs[1] = {{dq, qb, "dq"}};
-    if ((st = check_buffers(in, 5, outs, 1))) return st;
+    if ((st = check_buffers(in, 4, outs, 1))) return st;
     e = s2a::launch_bwd_dq(a, nullptr, s);
   }
   if (e != hipSuccess) return hip_fail(e, "backward stage");
@@ -260,8 +264,8 @@ size_t fwd_rope_ws(int B, int N, int H, int Hkv, int D) {
 
 size_t bwd_ws(int B, int N, int H, int Hkv, int D, bool rope) {
   if (B <= 0 || N <= 0 || H <= 0 || Hkv <= 0 || D <= 0) return 0;
-  size_t n = 2 * round_up(stat_bytes(B, N, H));
-  if (rope) n += round_up(q_bytes(B, N, H, D)) + round_up(q_bytes(B, N, Hkv, D));
+  size_t n = 2 * round_up(stat_bytes(B, N, H)) + round_up(q_bytes(B, N, H, D));
+  if (rope) n += round_up(q_bytes(B, N, Hkv, D));
   return n;
 }
 
@@ -285,28 +289,27 @@ int s2attn_bwd(const void* q, const void* k, const void* v, const void* out, con
   });
 }
 
-int s2attn_bwd_preprocess(const void* out, const void* dout, const float* lse, int B, int N, int H, int D,
-                          void* workspace, size_t workspace_bytes, void* stream) {
+int s2attn_bwd_preprocess(const void* q, const void* out, const void* dout, const float* lse, int B, int N, int H,
+                          int D, void* workspace, size_t workspace_bytes, void* stream) {
   return guarded([&] {
-    return do_bwd_stage(Stage::kPre, nullptr, nullptr, nullptr, out, lse, dout, nullptr, nullptr, nullptr, B, N,
-                        H, H, D, 1, 0, workspace, workspace_bytes, stream);
+    return do_bwd_stage(Stage::kPre, q, nullptr, nullptr, out, lse, dout, nullptr, nullptr, nullptr, B, N, H, H, D,
+                        1, 0, workspace, workspace_bytes, stream);
   });
 }
 
-int s2attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, void* dk, void* dv, int B, int N,
-                    int H, int Hkv, int D, int G, int shift, const void* workspace, size_t workspace_bytes,
-                    void* stream) {
+int s2attn_bwd_dkdv(const void* k, const void* v, const void* dout, void* dk, void* dv, int B, int N, int H,
+                    int Hkv, int D, int G, int shift, const void* workspace, size_t workspace_bytes, void* stream) {
   return guarded([&] {
-    return do_bwd_stage(Stage::kDkdv, q, k, v, nullptr, nullptr, dout, nullptr, dk, dv, B, N, H, Hkv, D, G, shift,
-                        workspace, workspace_bytes, stream);
+    return do_bwd_stage(Stage::kDkdv, nullptr, k, v, nullptr, nullptr, dout, nullptr, dk, dv, B, N, H, Hkv, D, G,
+                        shift, workspace, workspace_bytes, stream);
   });
 }
 
-int s2attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout, void* dq, int B, int N, int H,
-                  int Hkv, int D, int G, int shift, const void* workspace, size_t workspace_bytes, void* stream) {
+int s2attn_bwd_dq(const void* k, const void* v, const void* dout, void* dq, int B, int N, int H, int Hkv, int D,
+                  int G, int shift, const void* workspace, size_t workspace_bytes, void* stream) {
   return guarded([&] {
-    return do_bwd_stage(Stage::kDq, q, k, v, nullptr, nullptr, dout, dq, nullptr, nullptr, B, N, H, Hkv, D, G, shift,
-                        workspace, workspace_bytes, stream);
+    return do_bwd_stage(Stage::kDq, nullptr, k, v, nullptr, nullptr, dout, dq, nullptr, nullptr, B, N, H, Hkv, D, G,
+                        shift, workspace, workspace_bytes, stream);
   });
 }
 

@@ -116,15 +116,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const bool qvalid = qi < s.G;
   const int qpos = qvalid ? orig_pos(base, qi, s.N) : 0;
   const long long qoff = ((long long)(b * (long long)s.N + qpos) * s.H + h) * D;
-  // q scaled by c*log2(e) (as in the forward), so S comes out in log2 units.
+  // q arrives as q * c * log2(e) (the forward's rounding of it), so S comes
+  // out in log2 units.
   bf16x8 qf[D / 16], dof[D / 16];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
-    float x[8];
-    unpack8(qvalid ? ld16(a.q + qoff + kk * 16 + hh * 8) : zero_u4(), x);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] *= a.scale_log2;
-    qf[kk] = as_bf16x8(pack8(x));
+    u32x4 qw = qvalid ? ld16(a.q + qoff + kk * 16 + hh * 8) : zero_u4();
+    asm volatile("" : "+v"(qw));  // keep the fragment resident from here on
+    qf[kk] = as_bf16x8(qw);
     dof[kk] = as_bf16x8(qvalid ? ld16(a.dout + qoff + kk * 16 + hh * 8) : zero_u4());
   }
   const long long stat_off = ((long long)b * s.H + h) * s.N + qpos;
@@ -330,18 +329,11 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
   const bool kvalid = kj < s.G;
   const int kpos = kvalid ? orig_pos(base, kj, s.N) : 0;
   const long long koff = ((long long)b * s.N + kpos) * kv_row + (long long)kvh * D;
-  // The P wave's K is scaled by c*log2(e), so its S comes out in log2 units.
   const uint16_t* kv_src = ds_wave ? a.v : a.k;
-  const float kv_scale = ds_wave ? 1.f : a.scale_log2;
   bf16x8 kvf[D / 16];
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    float x[8];
-    unpack8(kvalid ? ld16(kv_src + koff + kk * 16 + hh * 8) : zero_u4(), x);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] *= kv_scale;
-    kvf[kk] = as_bf16x8(pack8(x));
-  }
+  for (int kk = 0; kk < D / 16; ++kk) kvf[kk] = as_bf16x8(kvalid ? ld16(kv_src + koff + kk * 16 + hh * 8) : zero_u4());
+
 
   f32x16 acc[D / 32];  // dV^T (P wave) or dK^T (dS wave)
 #pragma unroll
@@ -454,6 +446,28 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
     return v;
   };
 
+  // acc += T K^T (or T V^T) for the step's 32-row tile T in LDS: one
+  // dependent chain of D/16 MFMAs whose A fragments are read five k-steps
+  // ahead (the compiler would otherwise put each read right before its MFMA
+  // and expose the LDS latency at every k-step).
+  auto chain_mfma = [&](f32x16& acc_, const uint16_t* t) __attribute__((always_inline)) {
+    constexpr int kPF = 6;  // fragments in flight
+    bf16x8 fa[kPF];
+#pragma unroll
+    for (int kk = 0; kk < kPF - 1; ++kk) fa[kk] = sw.row(t, 0, kk);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      if (kk + kPF - 1 < D / 16) fa[(kk + kPF - 1) % kPF] = sw.row(t, 0, kk + kPF - 1);
+      acc_ = mfma32x32x16(fa[kk % kPF], kvf[kk], acc_);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, kPF - 1, 0);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      if (kk + kPF - 1 < D / 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+  };
+
   // P wave: S = Q K^T - lse (log2 units; lane column = key, elements = rows
   // 8*(r/4) + 4*hh + r%4 of the step), P = exp2(S), publish P,
   // dV^T += dO^T P.
@@ -463,15 +477,7 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
     const uint16_t* ot = obuf(c);
     const float* st = stats(c);
     f32x16 sc = row_stats(st);
-    {
-      bf16x8 qa[2];
-      qa[0] = sw.row(qt, 0, 0);
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        if (kk + 1 < D / 16) qa[(kk + 1) & 1] = sw.row(qt, 0, kk + 1);
-        sc = mfma32x32x16(qa[kk & 1], kvf[kk], sc);
-      }
-    }
+    chain_mfma(sc, qt);
     float p[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -504,15 +510,7 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
     const uint16_t* ot = obuf(c);
     const float* st = stats(c);
     f32x16 dp = row_stats(st + kBMQ);
-    {
-      bf16x8 oa[2];
-      oa[0] = sw.row(ot, 0, 0);
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        if (kk + 1 < D / 16) oa[(kk + 1) & 1] = sw.row(ot, 0, kk + 1);
-        dp = mfma32x32x16(oa[kk & 1], kvf[kk], dp);
-      }
-    }
+    chain_mfma(dp, ot);
     const bf16x8 pb0 = __builtin_bit_cast(bf16x8, Pbuf[step & 1][pair][0][lane]);
     const bf16x8 pb1 = __builtin_bit_cast(bf16x8, Pbuf[step & 1][pair][1][lane]);
     float ds[16];
@@ -608,7 +606,7 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
 
   if (kvalid) {
     if (ds_wave)
-      store_row_acc<D, ROPE>(a.dk + koff, acc, a.scale, hh, kpos, rope);
+      store_row_acc<D, ROPE>(a.dk + koff, acc, kLn2, hh, kpos, rope);  // q arrives scaled by c log2 e
     else
       store_row_acc<D, false>(a.dv + koff, acc, 1.f, hh, kpos, rope);
   }

@@ -7,8 +7,13 @@
 // Computing it once per row here spares the dK/dV pass (which visits every
 // row once per k/v tile) from re-reading O.  Storing both statistics negated
 // (and lse in log2 units) lets the later kernels use them as the start value
-// of the S and dP accumulators: P = exp2(acc), dS = P * acc.  HBM-bound:
-// reads out and dout once (16-byte coalesced loads), 8 bytes per row else.
+// of the S and dP accumulators: P = exp2(acc), dS = P * acc.
+// Without RoPE it also writes qs = bf16(q * c * log2(e)), the q operand of
+// the forward's logits (the forward scales its q rows the same way, in fp32
+// with one bf16 rounding): the backward kernels recompute P from exactly the
+// logits the forward normalised, so each row of P sums to one against the
+// saved lse.  HBM-bound: reads out, dout (and q) once with 16-byte coalesced
+// loads, 8 bytes per row else.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -20,7 +25,9 @@ namespace {
 template <int D>
 __global__ __launch_bounds__(256) void delta_kernel(const uint16_t* __restrict__ out, const uint16_t* __restrict__ dout,
                                                     const float* __restrict__ lse, float* __restrict__ ndelta,
-                                                    float* __restrict__ nlse2, long long rows, int N, int H) {
+                                                    float* __restrict__ nlse2, const uint16_t* __restrict__ q,
+                                                    uint16_t* __restrict__ qs, float scale, long long rows, int N,
+                                                    int H) {
   constexpr int CH = D / 8;  // lanes per row (16 or 8), a power of two dividing 64
   const long long item = (long long)blockIdx.x * 256 + threadIdx.x;
   const long long row = item / CH;  // (b*N + n)*H + h
@@ -31,6 +38,12 @@ __global__ __launch_bounds__(256) void delta_kernel(const uint16_t* __restrict__
     unpack8(ld16(dout + item * 8), y);
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc += x[e] * y[e];
+    if (q != nullptr) {
+      unpack8(ld16(q + item * 8), x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] *= scale;
+      st16(qs + item * 8, pack8(x));
+    }
   }
 #pragma unroll
   for (int off = CH / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
@@ -48,7 +61,8 @@ __global__ __launch_bounds__(256) void delta_kernel(const uint16_t* __restrict__
 }  // namespace
 
 hipError_t launch_bwd_delta(const uint16_t* out, const uint16_t* dout, const float* lse, float* ndelta,
-                            float* nlse2, const Shape& s, hipStream_t stream) {
+                            float* nlse2, const uint16_t* q, uint16_t* qs, float scale, const Shape& s,
+                            hipStream_t stream) {
   const long long rows = (long long)s.B * s.N * s.H;
   const long long total = rows * (s.D / 8);
   if (total == 0) return hipSuccess;
@@ -56,10 +70,10 @@ hipError_t launch_bwd_delta(const uint16_t* out, const uint16_t* dout, const flo
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (s.D == 64)
     hipLaunchKernelGGL(delta_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, stream, out, dout, lse, ndelta, nlse2,
-                       rows, s.N, s.H);
+                       q, qs, scale, rows, s.N, s.H);
   else
     hipLaunchKernelGGL(delta_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, stream, out, dout, lse, ndelta, nlse2,
-                       rows, s.N, s.H);
+                       q, qs, scale, rows, s.N, s.H);
   return hipGetLastError();
 }
 

@@ -32,7 +32,8 @@ struct FwdArgs {
 };
 
 struct BwdArgs {
-  const uint16_t* q;     // [B, N, H, D]   (rotated copy when rope is on)
+  const uint16_t* q;     // [B, N, H, D]: q * c * log2(e) in bf16 (rotated first when rope is on), the
+                         // operand the forward's logits used (written by the preprocess pass)
   const uint16_t* k;     // [B, N, Hkv, D] (rotated copy when rope is on)
   const uint16_t* v;
   const uint16_t* dout;  // [B, N, H, D]
@@ -49,12 +50,15 @@ struct BwdArgs {
 
 // Launchers: enqueue on `stream`, return the HIP status of the launch.
 hipError_t launch_fwd(const FwdArgs& a, const RopeTable* rope, hipStream_t stream);
+// Also writes qs = bf16(q * scale) when q is non-null (q and qs [B, N, H, D]).
 hipError_t launch_bwd_delta(const uint16_t* out, const uint16_t* dout, const float* lse, float* ndelta,
-                            float* nlse2, const Shape& s, hipStream_t stream);
+                            float* nlse2, const uint16_t* q, uint16_t* qs, float scale, const Shape& s,
+                            hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, const RopeTable* rope, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, const RopeTable* rope, hipStream_t stream);
-// Rotate rows*heads*D bf16 values of a [B, N, heads, D] tensor into dst.
+// Rotate rows*heads*D bf16 values of a [B, N, heads, D] tensor into dst,
+// multiplying by `scale` after the rotation (one bf16 rounding).
 hipError_t launch_rope_rotate(const uint16_t* src, uint16_t* dst, const Shape& s, int heads,
-                              const RopeTable& rope, hipStream_t stream);
+                              const RopeTable& rope, float scale, hipStream_t stream);
 
 }  // namespace s2a

@@ -7,8 +7,10 @@
 // Operands that the attention kernels stream many times (k in the forward
 // and dQ passes, q in the dK/dV pass) are rotated here once instead of once
 // per reuse; operands read once per workgroup are rotated inside the
-// attention kernels with the same device routine.  Memory-bound: one 16-byte
-// load and store per thread, coalesced along D.
+// attention kernels with the same device routine.  The backward's q copy is
+// also multiplied by c log2(e) here, in the same fp32 operations and order as
+// the forward applies to its q rows, so both passes see identical logits.
+// Memory-bound: one 16-byte load and store per thread, coalesced along D.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -18,7 +20,8 @@ namespace {
 
 template <int D>
 __global__ __launch_bounds__(256) void rope_kernel(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
-                                                   long long rows, int N, int heads, RopeTable rope) {
+                                                   long long rows, int N, int heads, RopeTable rope,
+                                                   float scale) {
   constexpr int CH = D / 8;
   const long long item = (long long)blockIdx.x * 256 + threadIdx.x;
   const long long total = rows * heads * CH;
@@ -29,22 +32,28 @@ __global__ __launch_bounds__(256) void rope_kernel(const uint16_t* __restrict__ 
   float x[8];
   unpack8(ld16(src + item * 8), x);
   rope_rotate8(x, pos, rope.rev, ch * 8, false);
+  if (scale != 1.f) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] *= scale;
+  }
   st16(dst + item * 8, pack8(x));
 }
 
 }  // namespace
 
 hipError_t launch_rope_rotate(const uint16_t* src, uint16_t* dst, const Shape& s, int heads,
-                              const RopeTable& rope, hipStream_t stream) {
+                              const RopeTable& rope, float scale, hipStream_t stream) {
   const long long rows = (long long)s.B * s.N;
   const long long total = rows * heads * (s.D / 8);
   if (total == 0) return hipSuccess;
   const long long blocks = (total + 255) / 256;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (s.D == 64)
-    hipLaunchKernelGGL(rope_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, stream, src, dst, rows, s.N, heads, rope);
+    hipLaunchKernelGGL(rope_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, stream, src, dst, rows, s.N, heads, rope,
+                       scale);
   else
-    hipLaunchKernelGGL(rope_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, stream, src, dst, rows, s.N, heads, rope);
+    hipLaunchKernelGGL(rope_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, stream, src, dst, rows, s.N, heads, rope,
+                       scale);
   return hipGetLastError();
 }
 

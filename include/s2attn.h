@@ -66,7 +66,10 @@ int s2attn_fwd(const void* q, const void* k, const void* v, void* out, float* ls
 
 /*
  * Workspace bytes s2attn_bwd needs: two float32 [B, H, N] row statistics,
- * -Delta[b, h, n] = -sum_d dout * out and -lse[b, h, n] * log2(e), each
+ * -Delta[b, h, n] = -sum_d dout * out and -lse[b, h, n] * log2(e), then a
+ * bf16 [B, N, H, D] copy of q * log2(e) / sqrt(D) (the q operand of the
+ * forward's logits, rounded as the forward rounds it, so the backward
+ * recomputes P from exactly the logits the forward normalised), each
  * starting on a 256-byte boundary.
  */
 size_t s2attn_bwd_workspace_size(int B, int N, int H, int Hkv, int D);
@@ -88,22 +91,23 @@ int s2attn_bwd(const void* q, const void* k, const void* v, const void* out, con
  * The backward in stages: the same kernels s2attn_bwd enqueues, in the same
  * order, for callers that want to schedule or time them separately.
  *   s2attn_bwd_preprocess  the row statistics (-Delta, -lse*log2(e)) from
- *                          out, dout and the forward's lse into the workspace
- *   s2attn_bwd_dkdv        dk, dv (reads the statistics)
- *   s2attn_bwd_dq          dq     (reads the statistics)
+ *                          out, dout and the forward's lse, and the scaled
+ *                          copy of q, into the workspace
+ *   s2attn_bwd_dkdv        dk, dv (reads the workspace, not q)
+ *   s2attn_bwd_dq          dq     (reads the workspace, not q)
  * dkdv and dq do not depend on each other and may run on different streams
  * once preprocess has completed.  Arguments and the workspace are those of
  * s2attn_bwd (workspace of s2attn_bwd_workspace_size() bytes); dkdv and dq
  * only read the workspace.
  */
-int s2attn_bwd_preprocess(const void* out, const void* dout, const float* lse,
+int s2attn_bwd_preprocess(const void* q, const void* out, const void* dout, const float* lse,
                           int B, int N, int H, int D,
                           void* workspace, size_t workspace_bytes, void* stream);
-int s2attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
+int s2attn_bwd_dkdv(const void* k, const void* v, const void* dout,
                     void* dk, void* dv,
                     int B, int N, int H, int Hkv, int D, int G, int shift,
                     const void* workspace, size_t workspace_bytes, void* stream);
-int s2attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout, void* dq,
+int s2attn_bwd_dq(const void* k, const void* v, const void* dout, void* dq,
                   int B, int N, int H, int Hkv, int D, int G, int shift,
                   const void* workspace, size_t workspace_bytes, void* stream);
 
@@ -128,7 +132,8 @@ int s2attn_fwd_rope(const void* q, const void* k, const void* v, void* out, floa
 /*
  * Backward of s2attn_fwd_rope: dq and dk are gradients w.r.t. the unrotated
  * q and k (passed back through the transposed rotation).  The workspace holds
- * Delta plus rotated copies of q and k.
+ * the two row statistics, the rotated q times log2(e) / sqrt(D) and the
+ * rotated k.
  */
 size_t s2attn_bwd_rope_workspace_size(int B, int N, int H, int Hkv, int D);
 int s2attn_bwd_rope(const void* q, const void* k, const void* v, const void* out,

@@ -124,7 +124,8 @@ def test_bwd_checks_workspace():
     L = _lib.lib()
     B, N, H, Hkv, D, G, sh = 1, 256, 4, 4, 64, 64, 32
     need = L.s2attn_bwd_workspace_size(B, N, H, Hkv, D)
-    assert need >= 2 * B * H * N * 4 and need % 256 == 0  # -Delta and -lse*log2(e)
+    # -Delta and -lse*log2(e) (fp32), then the scaled copy of q (bf16)
+    assert need >= 2 * B * H * N * 4 + B * N * H * D * 2 and need % 256 == 0
     step = 1 << 24
     p = [0x10000000 + i * step for i in range(10)]
     st = L.s2attn_bwd(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7], p[8], B, N, H, Hkv, D, G, sh,
@@ -149,8 +150,8 @@ def test_workspace_sizes():
     br = L.s2attn_bwd_rope_workspace_size(B, N, H, Hkv, D)
     b = L.s2attn_bwd_workspace_size(B, N, H, Hkv, D)
     assert fr >= B * N * Hkv * D * 2
-    assert b >= 2 * B * H * N * 4
-    assert br >= b + B * N * (H + Hkv) * D * 2
+    assert b >= 2 * B * H * N * 4 + B * N * H * D * 2
+    assert br >= b + B * N * Hkv * D * 2  # plus the rotated k
     assert L.s2attn_bwd_workspace_size(0, N, H, Hkv, D) == 0
 
 

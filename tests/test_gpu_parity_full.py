@@ -169,3 +169,42 @@ def test_llama2_7b_100k_backward_units(kvh, g):
 
 def test_llama2_7b_100k_gradient_invariants():
     run_of("llama2_7b_n100k").check_gradient_invariants()
+
+
+# ------------------------------------------- dense causal (inference mode)
+
+@pytest.mark.parametrize("h", [0, 31])
+def test_dense_32k_forward_units(h):
+    run_of("llama2_7b_dense_n32k").check_forward_unit(h, 0)
+
+
+def test_dense_32k_backward_unit():
+    run_of("llama2_7b_dense_n32k").check_backward_kv_group(16, 0)
+
+
+def test_dense_32k_gradient_invariants():
+    run_of("llama2_7b_dense_n32k").check_gradient_invariants()
+
+
+# ------------------------------- RoPE scaling: PI by 25 at 100k, base x 8
+
+@pytest.mark.parametrize("h,g", [(0, 0), (31, 3)])
+def test_rope_pi25_100k_forward_units(h, g):
+    run_of("llama2_7b_n100k_rope_pi25").check_forward_unit(h, g)
+
+
+def test_rope_pi25_100k_backward_unit():
+    run_of("llama2_7b_n100k_rope_pi25").check_backward_kv_group(31, 3)
+
+
+def test_rope_pi25_100k_gradient_invariants():
+    run_of("llama2_7b_n100k_rope_pi25").check_gradient_invariants()
+
+
+@pytest.mark.parametrize("h,g", [(3, 1), (20, 3)])
+def test_rope_base8_32k_forward_units(h, g):
+    run_of("llama2_7b_n32k_rope_base8").check_forward_unit(h, g)
+
+
+def test_rope_base8_32k_backward_unit():
+    run_of("llama2_7b_n32k_rope_base8").check_backward_kv_group(20, 3)

@@ -33,6 +33,12 @@ CASES = [
     ("g2048_large_tiles", 1, 4096, 2, 2, 128, 2048, 1024, None),
     ("ragged_g1100_large_tiles", 1, 2200, 2, 2, 64, 1100, 550, None),
     ("gqa_rope_g1536", 1, 3072, 4, 2, 128, 1536, 768, (10000.0, 8.0)),
+    # RoPE scaling variants: position interpolation by 25 out to 100k
+    # positions, and the base scaled by 8; dense causal through the
+    # eight-wave kernel.
+    ("rope_pi25_to_100k", 1, 102400, 2, 2, 128, 4096, 2048, (10000.0, 25.0)),
+    ("rope_base8_gqa", 1, 2048, 4, 2, 128, 512, 256, (80000.0, 1.0)),
+    ("dense_g4096_large_tiles", 1, 4096, 2, 2, 128, 4096, 0, None),
 ]
 IDS = [c[0] for c in CASES]
 
@@ -208,9 +214,9 @@ def test_backward_stages_equal_the_composite_call():
     out, lse = ops.s2attn_fwd(q, k, v, G, sh)
     dq, dk, dv = ops.s2attn_bwd(q, k, v, out, lse, do, G, sh)
     ws = ops.bwd_workspace(q, k)
-    ops.s2attn_bwd_preprocess(out, do, lse, ws)
-    dk2, dv2 = ops.s2attn_bwd_dkdv(q, k, v, do, G, sh, ws)
-    dq2 = ops.s2attn_bwd_dq(q, k, v, do, G, sh, ws)
+    ops.s2attn_bwd_preprocess(q, out, do, lse, ws)
+    dk2, dv2 = ops.s2attn_bwd_dkdv(k, v, do, G, sh, ws)
+    dq2 = ops.s2attn_bwd_dq(k, v, do, G, sh, ws)
     torch.cuda.synchronize()
     for a, b in ((dq, dq2), (dk, dk2), (dv, dv2)):
         assert np.array_equal(to_bits(a), to_bits(b))

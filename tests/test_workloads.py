@@ -44,7 +44,10 @@ def test_draws_are_seeded_and_ordered():
 def test_workload_shapes_are_consistent():
     for name, c in workloads.WORKLOADS.items():
         assert c["N"] % c["G"] == 0, name
-        assert c["shift"] == c["G"] // 2, name
         assert c["H"] % c["Hkv"] == 0 and c["H"] % 2 == 0 and c["Hkv"] % 2 == 0, name
-        assert c["G"] * 4 == c["N"], name  # G = N/4 throughout
+        if c["G"] == c["N"]:
+            assert c["shift"] == 0, name  # dense causal: one group, nothing to shift
+        else:
+            assert c["shift"] == c["G"] // 2, name
+            assert c["G"] * 4 == c["N"], name  # G = N/4 for every S2-Attn shape
     assert workloads.BENCH_WORKLOAD in workloads.WORKLOADS

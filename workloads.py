@@ -26,6 +26,15 @@ WORKLOADS = {
     "llama2_7b_n100k": dict(B=1, N=102400, H=32, Hkv=32, D=128, G=25600, shift=12800, rope=None),
     "llama2_70b_gqa_n32k_rope": dict(B=1, N=32768, H=64, Hkv=8, D=128, G=8192, shift=4096,
                                      rope=(10000.0, 8.0)),
+    # Dense causal attention (one group, no shift): the inference mode the
+    # pages switch back to after S2-Attn fine-tuning.
+    "llama2_7b_dense_n32k": dict(B=1, N=32768, H=32, Hkv=32, D=128, G=32768, shift=0, rope=None),
+    # 100k context with position interpolation by s = 25 (a 4k model
+    # stretched to 100k), and 32k with the RoPE base scaled by 8 instead.
+    "llama2_7b_n100k_rope_pi25": dict(B=1, N=102400, H=32, Hkv=32, D=128, G=25600, shift=12800,
+                                      rope=(10000.0, 25.0)),
+    "llama2_7b_n32k_rope_base8": dict(B=1, N=32768, H=32, Hkv=32, D=128, G=8192, shift=4096,
+                                      rope=(80000.0, 1.0)),
 }
 
 # The workload the benchmark times: LLaMA2-7B attention at 32k context.
