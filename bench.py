@@ -17,8 +17,9 @@ Prints ONE JSON line.  Options:
   --gpus N        only 1 is supported (the path is single-GPU)
   --steps K       timed steps (default 20)
   --warmup W      untimed steps first (default 5)
-  --workload W    a key of workloads.WORKLOADS (with RoPE: the fused entry
-                  points are timed as two units, forward and backward)
+  --workload W    a key of workloads.WORKLOADS (with RoPE or alternate-head
+                  shifting: the general entry points are timed as two calls,
+                  forward and backward)
   --no-cpu-baseline   skip timing the fp64 oracle on a sample
   --calib-copy-mib M  also run one plain device copy of M MiB (for counter calibration)
 """
@@ -70,7 +71,7 @@ def cpu_baseline(cfg, x_bits, budget_s=20.0):
         kvh = oracle.kv_head(h, H, Hkv)
         f64 = lambda name, hh: workloads.f64_from_bf16_bits(x_bits[name][0, :, hh, :])
         qh, kh, vh, doh = f64("q", h), f64("k", kvh), f64("v", kvh), f64("dout", h)
-        shh = oracle.head_shift(h, H, sh)
+        shh = oracle.head_shift(h, H, sh, cfg.get("head_pattern", "second_half"), Hkv)
         oracle.head_unit_forward(qh, kh, vh, G, shh, g, rope=cfg["rope"])
         oracle.head_unit_backward(qh, kh, vh, doh, G, shh, g, rope=cfg["rope"])
         done += 1
@@ -119,6 +120,8 @@ def main():
     name = args.workload or workloads.BENCH_WORKLOAD
     cfg = dict(workloads.WORKLOADS[name], name=name)
     rope = cfg["rope"]
+    pattern = cfg.get("head_pattern", "second_half")
+    fused = rope is not None or pattern != "second_half"
     B, N, H, Hkv, D, G, sh = (cfg[k] for k in ("B", "N", "H", "Hkv", "D", "G", "shift"))
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
@@ -144,25 +147,26 @@ def main():
         del src, dst
 
     kernels = ["fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq"]
-    if rope is not None:
-        # The fused RoPE entry points have no stage calls: time the forward
-        # (k rotation + attention) and the backward (q, k rotations, the
-        # statistics pass, dK/dV, dQ) as whole calls.
-        kernels = ["fwd_rope", "bwd_rope"]
+    if fused:
+        # The general entry points have no stage calls: time the forward
+        # (with its k rotation) and the backward (rotations or q scaling,
+        # the statistics pass, dK/dV, dQ) as whole calls.
+        kernels = ["fwd_call", "bwd_call"]
 
-    def step_rope(events=None):
+    def step_fused(events=None):
         if events is not None:
             events[0].record(stream)
-        ops.s2attn_fwd_rope(q, k, v, G, sh, *rope, out=out, lse=lse, workspace=ws_f)
+        ops.s2attn_fwd_ex(q, k, v, G, sh, head_pattern=pattern, rope=rope, out=out, lse=lse, workspace=ws_f)
         if events is not None:
             events[1].record(stream)
-        ops.s2attn_bwd_rope(q, k, v, out, lse, do, G, sh, *rope, dq=dq, dk=dk, dv=dv, workspace=ws)
+        ops.s2attn_bwd_ex(q, k, v, out, lse, do, G, sh, head_pattern=pattern, rope=rope, dq=dq, dk=dk, dv=dv,
+                          workspace=ws)
         if events is not None:
             events[2].record(stream)
 
     def step(events=None):
-        if rope is not None:
-            return step_rope(events)
+        if fused:
+            return step_fused(events)
         if events is not None:
             events[0].record(stream)
         ops.s2attn_fwd(q, k, v, G, sh, out=out, lse=lse)
@@ -200,8 +204,8 @@ def main():
     # forward 2 products, dK/dV 4 (S, dP, dV, dK), dQ 3 (S, dP, dQ).
     unit = B * H * N * G * D
     kernel_flops = {"fwd": 2 * unit, "bwd_dkdv": 4 * unit, "bwd_dq": 3 * unit}
-    if rope is not None:
-        kernel_flops = {"fwd_rope": 2 * unit, "bwd_rope": 7 * unit}
+    if fused:
+        kernel_flops = {"fwd_call": 2 * unit, "bwd_call": 7 * unit}
     dominant = max(kernel_flops, key=lambda kname: kernel_ms[kname])
     achieved = kernel_flops[dominant] / (kernel_ms[dominant] * 1e-3) / 1e12
     roofline = {
@@ -231,7 +235,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": name, "B": B, "N": N, "H": H, "Hkv": Hkv, "D": D, "G": G, "shift": sh,
-                   "rope": list(rope) if rope is not None else None, "parallelism": "single-gpu"},
+                   "rope": list(rope) if rope is not None else None, "head_pattern": pattern,
+                   "parallelism": "single-gpu"},
         "pct_peak": 100.0 * value / PEAK_BF16_TFLOPS,
         "fwd_tflops": f_fwd / (kernel_ms[kernels[0]] * 1e-3) / 1e12,
         "bwd_tflops": f_bwd / (sum(kernel_ms[kk] for kk in kernels[1:]) * 1e-3) / 1e12,

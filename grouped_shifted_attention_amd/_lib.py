@@ -14,6 +14,8 @@ S2ATTN_OK = 0
 S2ATTN_EINVAL = -1
 S2ATTN_EUNSUPPORTED = -2
 S2ATTN_EHIP = -3
+S2ATTN_HEADS_SECOND_HALF = 0
+S2ATTN_HEADS_ALTERNATE = 1
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -33,6 +35,9 @@ SIGNATURES = {
     "s2attn_bwd_rope_workspace_size": (_S, [_I, _I, _I, _I, _I]),
     "s2attn_bwd_rope": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _D, _D,
                              _P, _S, _P]),
+    "s2attn_fwd_ex": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _D, _D, _P, _S, _P]),
+    "s2attn_bwd_ex": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _D, _D,
+                           _P, _S, _P]),
     "s2attn_strerror": (ctypes.c_char_p, [_I]),
     "s2attn_last_error": (ctypes.c_char_p, []),
 }

@@ -39,14 +39,16 @@ constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Shape rules.  Returns S2ATTN_OK or an error status (message recorded).
-int check_shape(int B, int N, int H, int Hkv, int D, int G, int shift) {
+int check_shape(int B, int N, int H, int Hkv, int D, int G, int shift, int pattern = S2ATTN_HEADS_SECOND_HALF) {
   if (B < 0 || N < 0) return fail(S2ATTN_EINVAL, "B and N must be >= 0");
   if (H < 1 || Hkv < 1) return fail(S2ATTN_EINVAL, "H and Hkv must be >= 1");
   if (H % Hkv != 0) return fail(S2ATTN_EINVAL, "H must be a multiple of Hkv");
   if (G < 1) return fail(S2ATTN_EINVAL, "G must be >= 1");
   if (N % G != 0) return fail(S2ATTN_EINVAL, "N must be a multiple of G");
   if (shift < 0 || shift >= G) return fail(S2ATTN_EINVAL, "shift must lie in [0, G)");
-  if (shift > 0 && (H % 2 != 0 || Hkv % 2 != 0))
+  if (pattern != S2ATTN_HEADS_SECOND_HALF && pattern != S2ATTN_HEADS_ALTERNATE)
+    return fail(S2ATTN_EINVAL, "head_pattern must be S2ATTN_HEADS_SECOND_HALF or S2ATTN_HEADS_ALTERNATE");
+  if (pattern == S2ATTN_HEADS_SECOND_HALF && shift > 0 && (H % 2 != 0 || Hkv % 2 != 0))
     return fail(S2ATTN_EINVAL, "with shift > 0, H and Hkv must be even (heads split in halves)");
   if (D < 1) return fail(S2ATTN_EINVAL, "D must be >= 1");
   if (D != 64 && D != 128) return fail(S2ATTN_EUNSUPPORTED, "D must be 64 or 128");
@@ -104,16 +106,17 @@ s2a::RopeTable make_rope(int D, double base, double pos_scale) {
   return t;
 }
 
-s2a::Shape make_shape(int B, int N, int H, int Hkv, int D, int G, int shift) {
-  return s2a::Shape{B, N, H, Hkv, D, G, shift, G > 0 ? N / G : 0};
+s2a::Shape make_shape(int B, int N, int H, int Hkv, int D, int G, int shift, int pattern) {
+  return s2a::Shape{B, N, H, Hkv, D, G, shift, G > 0 ? N / G : 0, pattern};
 }
 
 size_t q_bytes(int B, int N, int H, int D) { return (size_t)B * N * H * D * 2; }
 size_t stat_bytes(int B, int N, int H) { return (size_t)B * H * N * 4; }
 
 int do_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int N, int H, int Hkv,
-           int D, int G, int shift, const double* rope, void* ws, size_t ws_bytes, void* stream) {
-  int st = check_shape(B, N, H, Hkv, D, G, shift);
+           int D, int G, int shift, const double* rope, void* ws, size_t ws_bytes, void* stream,
+           int pattern = S2ATTN_HEADS_SECOND_HALF) {
+  int st = check_shape(B, N, H, Hkv, D, G, shift, pattern);
   if (st) return st;
   if (rope && (st = check_rope(rope[0], rope[1]))) return st;
   if (B == 0 || N == 0) return S2ATTN_OK;
@@ -134,7 +137,7 @@ int do_fwd(const void* q, const void* k, const void* v, void* out, float* lse, i
   a.v = (const uint16_t*)v;
   a.out = (uint16_t*)out;
   a.lse = lse;
-  a.s = make_shape(B, N, H, Hkv, D, G, shift);
+  a.s = make_shape(B, N, H, Hkv, D, G, shift, pattern);
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
   hipError_t e;
   if (rope) {
@@ -151,8 +154,8 @@ int do_fwd(const void* q, const void* k, const void* v, void* out, float* lse, i
 
 int do_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse, const void* dout,
            void* dq, void* dk, void* dv, int B, int N, int H, int Hkv, int D, int G, int shift, const double* rope,
-           void* ws, size_t ws_bytes, void* stream) {
-  int st = check_shape(B, N, H, Hkv, D, G, shift);
+           void* ws, size_t ws_bytes, void* stream, int pattern = S2ATTN_HEADS_SECOND_HALF) {
+  int st = check_shape(B, N, H, Hkv, D, G, shift, pattern);
   if (st) return st;
   if (rope && (st = check_rope(rope[0], rope[1]))) return st;
   if (B == 0 || N == 0) return S2ATTN_OK;
@@ -180,7 +183,7 @@ int do_bwd(const void* q, const void* k, const void* v, const void* out, const f
   a.dq = (uint16_t*)dq;
   a.dk = (uint16_t*)dk;
   a.dv = (uint16_t*)dv;
-  a.s = make_shape(B, N, H, Hkv, D, G, shift);
+  a.s = make_shape(B, N, H, Hkv, D, G, shift, pattern);
   a.scale = (float)(1.0 / std::sqrt((double)D));
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
   hipError_t e;
@@ -209,6 +212,7 @@ enum class Stage { kPre, kDkdv, kDq };
 int do_bwd_stage(Stage stage, const void* q, const void* k, const void* v, const void* out, const float* lse,
                  const void* dout, void* dq, void* dk, void* dv, int B, int N, int H, int Hkv, int D, int G,
                  int shift, const void* ws, size_t ws_bytes, void* stream) {
+  const int pattern = S2ATTN_HEADS_SECOND_HALF;
   int st = check_shape(B, N, H, Hkv, D, G, shift);
   if (st) return st;
   if (B == 0 || N == 0) return S2ATTN_OK;
@@ -231,7 +235,7 @@ int do_bwd_stage(Stage stage, const void* q, const void* k, const void* v, const
   a.dq = (uint16_t*)dq;
   a.dk = (uint16_t*)dk;
   a.dv = (uint16_t*)dv;
-  a.s = make_shape(B, N, H, Hkv, D, G, shift);
+  a.s = make_shape(B, N, H, Hkv, D, G, shift, pattern);
   a.scale = (float)(1.0 / std::sqrt((double)D));
   a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)D));
   hipError_t e = hipSuccess;
@@ -334,6 +338,27 @@ int s2attn_bwd_rope(const void* q, const void* k, const void* v, const void* out
   return guarded([&] {
     return do_bwd(q, k, v, out, lse, dout, dq, dk, dv, B, N, H, Hkv, D, G, shift, rope, workspace,
                   workspace_bytes, stream);
+  });
+}
+
+int s2attn_fwd_ex(const void* q, const void* k, const void* v, void* out, float* lse, int B, int N, int H,
+                  int Hkv, int D, int G, int shift, int head_pattern, double rope_base, double pos_scale,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  const double rope[2] = {rope_base, pos_scale};
+  return guarded([&] {
+    return do_fwd(q, k, v, out, lse, B, N, H, Hkv, D, G, shift, rope_base != 0.0 ? rope : nullptr, workspace,
+                  workspace_bytes, stream, head_pattern);
+  });
+}
+
+int s2attn_bwd_ex(const void* q, const void* k, const void* v, const void* out, const float* lse, const void* dout,
+                  void* dq, void* dk, void* dv, int B, int N, int H, int Hkv, int D, int G, int shift,
+                  int head_pattern, double rope_base, double pos_scale, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  const double rope[2] = {rope_base, pos_scale};
+  return guarded([&] {
+    return do_bwd(q, k, v, out, lse, dout, dq, dk, dv, B, N, H, Hkv, D, G, shift,
+                  rope_base != 0.0 ? rope : nullptr, workspace, workspace_bytes, stream, head_pattern);
   });
 }
 

@@ -104,7 +104,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int bh = unit / s.NG;
   const int h = bh % s.H;
   const int b = bh / s.H;
-  const int sh = (h >= (s.H >> 1)) ? s.shift : 0;
+  const int sh = head_shift(h, s);
   const int kvh = h / (s.H / s.Hkv);
   const int base = g * s.G + sh;
   const long long kv_row = (long long)s.Hkv * D;
@@ -317,7 +317,7 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
   const int b = bk / s.Hkv;
   const int rq = s.H / s.Hkv;  // q heads per k/v head
   const int h0 = kvh * rq;
-  const int sh = (h0 >= (s.H >> 1)) ? s.shift : 0;  // shared by all rq q heads
+  const int sh = head_shift(h0, s);  // shared by all rq q heads
   const int base = g * s.G + sh;
   const long long kv_row = (long long)s.Hkv * D;
   const long long q_row = (long long)s.H * D;

@@ -11,6 +11,8 @@
 // read with ds_read_b64_tr_b16 in that permuted row order).
 #pragma once
 
+#include "kernels.hpp"
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -82,6 +84,17 @@ __device__ __forceinline__ int xcd_logical_id(int id, int total) {
   const int per = total / kXcds, rem = total % kXcds;
   const int xcd = id % kXcds, local = id / kXcds;
   return xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+}
+
+// Shift of q head h.  Pattern 0: the second half of the heads (h >= H/2)
+// is shifted ("LongLoRA and Shifted Sparse Attention (S^2-Attn)", opening
+// definition).  Pattern 1: alternate heads ("LoRA for Long-Context
+// Adaptation", section "Shifted sparse attention"), read as the q heads of
+// the odd k/v heads, which is the odd heads without sharing and keeps every
+// k/v head's rows rolled one way.
+__device__ __forceinline__ int head_shift(int h, const Shape& s) {
+  const bool shifted = s.pattern ? ((h / (s.H / s.Hkv)) & 1) != 0 : h >= (s.H >> 1);
+  return shifted ? s.shift : 0;
 }
 
 // Original sequence position of local row j of a group whose first rolled

@@ -74,7 +74,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 2
   const int bh = unit / s.NG;
   const int h = bh % s.H;
   const int b = bh / s.H;
-  const int sh = (h >= (s.H >> 1)) ? s.shift : 0;
+  const int sh = head_shift(h, s);
   const int kvh = h / (s.H / s.Hkv);
   const int base = g * s.G + sh;
   const long long kv_row = (long long)s.Hkv * D;
@@ -376,7 +376,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int bh = unit / s.NG;
   const int h = bh % s.H;
   const int b = bh / s.H;
-  const int sh = (h >= (s.H >> 1)) ? s.shift : 0;
+  const int sh = head_shift(h, s);
   const int kvh = h / (s.H / s.Hkv);
   const int base = g * s.G + sh;
   const long long kv_row = (long long)s.Hkv * D;

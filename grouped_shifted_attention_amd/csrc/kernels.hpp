@@ -11,7 +11,8 @@ namespace s2a {
 // head's causal attention inside one group of G rolled rows.
 struct Shape {
   int B, N, H, Hkv, D, G, shift;
-  int NG;  // groups per head, N / G
+  int NG;       // groups per head, N / G
+  int pattern;  // which heads are shifted: 0 the second half, 1 alternate k/v heads (see head_shift)
 };
 
 // Frequencies of the RoPE pairs in revolutions per position:

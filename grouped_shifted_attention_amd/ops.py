@@ -176,6 +176,54 @@ def s2attn_bwd_rope(q, k, v, out, lse, dout, G, shift, rope_base, pos_scale, dq=
     return dq, dk, dv
 
 
+HEAD_PATTERNS = {"second_half": 0, "alternate": 1}
+
+
+def _pattern(head_pattern):
+    if head_pattern not in HEAD_PATTERNS:
+        raise ValueError(f"head_pattern must be one of {sorted(HEAD_PATTERNS)}, got {head_pattern!r}")
+    return HEAD_PATTERNS[head_pattern]
+
+
+def s2attn_fwd_ex(q, k, v, G, shift, head_pattern="second_half", rope=None, out=None, lse=None, with_lse=True,
+                  workspace=None):
+    """Forward with every option: which heads are shifted ("second_half" or
+    "alternate") and, when ``rope`` is a (base, pos_scale) pair, RoPE with
+    position interpolation."""
+    B, N, H, Hkv, D = _dims(q, k, v)
+    out = torch.empty_like(q) if out is None else out
+    _need(out, "out", torch.bfloat16, (B, N, H, D), q.device)
+    if with_lse:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+        _need(lse, "lse", torch.float32, (B, H, N), q.device)
+    else:
+        lse = None
+    L = lib()
+    base, scale = (0.0, 1.0) if rope is None else (float(rope[0]), float(rope[1]))
+    ws = workspace
+    if ws is None and rope is not None:
+        ws = _workspace(L.s2attn_fwd_rope_workspace_size(B, N, H, Hkv, D), q.device)
+    check(L.s2attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, N, H, Hkv, D, int(G), int(shift),
+                          _pattern(head_pattern), base, scale, _ptr(ws),
+                          0 if ws is None else ws.numel() * ws.element_size(), _stream(q)))
+    return out, lse
+
+
+def s2attn_bwd_ex(q, k, v, out, lse, dout, G, shift, head_pattern="second_half", rope=None, dq=None, dk=None,
+                  dv=None, workspace=None):
+    """Backward of s2attn_fwd_ex (same head_pattern and rope)."""
+    (B, N, H, Hkv, D), dq, dk, dv = _bwd_common(q, k, v, out, lse, dout, dq, dk, dv)
+    L = lib()
+    base, scale = (0.0, 1.0) if rope is None else (float(rope[0]), float(rope[1]))
+    size = L.s2attn_bwd_workspace_size if rope is None else L.s2attn_bwd_rope_workspace_size
+    ws = _workspace(size(B, N, H, Hkv, D), q.device) if workspace is None else workspace
+    check(L.s2attn_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout),
+                          _ptr(dq), _ptr(dk), _ptr(dv), B, N, H, Hkv, D, int(G), int(shift),
+                          _pattern(head_pattern), base, scale,
+                          _ptr(ws), ws.numel() * ws.element_size(), _stream(q)))
+    return dq, dk, dv
+
+
 def bwd_workspace(q, k, rope=False):
     """A workspace tensor large enough for s2attn_bwd and its stages (or for
     s2attn_bwd_rope when rope is true)."""

@@ -56,6 +56,10 @@ extern "C" {
 #define S2ATTN_EUNSUPPORTED (-2)
 #define S2ATTN_EHIP (-3)
 
+/* Which q heads are shifted (s2attn_fwd_ex / s2attn_bwd_ex). */
+#define S2ATTN_HEADS_SECOND_HALF 0 /* heads H/2 .. H-1, as every other entry point does */
+#define S2ATTN_HEADS_ALTERNATE 1   /* the q heads of the odd k/v heads */
+
 /*
  * Forward pass.  Writes out (and lse unless lse is NULL).
  * Reads q, k, v; the group split and the rolls are folded into index
@@ -141,6 +145,36 @@ int s2attn_bwd_rope(const void* q, const void* k, const void* v, const void* out
                     int B, int N, int H, int Hkv, int D, int G, int shift,
                     double rope_base, double pos_scale,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The general entry points: every option of the calls above, plus the choice
+ * of shifted heads.
+ *   head_pattern  S2ATTN_HEADS_SECOND_HALF: heads H/2 .. H-1 are shifted
+ *                 ("LongLoRA and Shifted Sparse Attention (S^2-Attn)",
+ *                 opening definition; needs even H and Hkv when shift > 0).
+ *                 S2ATTN_HEADS_ALTERNATE: alternate heads are shifted ("LoRA
+ *                 for Long-Context Adaptation", section "Shifted sparse
+ *                 attention": heads 1, 3, 5, ...).  With grouped-query
+ *                 sharing this reads as the q heads of the odd k/v heads, so
+ *                 each k/v head's rows are rolled one way; without sharing it
+ *                 is exactly the odd heads.
+ *   rope_base     0 for no RoPE; otherwise RoPE with position interpolation
+ *                 as in s2attn_fwd_rope (rope_base > 0, pos_scale > 0, finite).
+ * Workspaces: the forward needs s2attn_fwd_rope_workspace_size() bytes when
+ * RoPE is on and none otherwise (workspace may be NULL); the backward needs
+ * s2attn_bwd_rope_workspace_size() or s2attn_bwd_workspace_size() bytes.
+ * Everything else (layouts, ownership, errors) is as for s2attn_fwd and
+ * s2attn_bwd; the backward must be given the forward's head_pattern and RoPE.
+ */
+int s2attn_fwd_ex(const void* q, const void* k, const void* v, void* out, float* lse,
+                  int B, int N, int H, int Hkv, int D, int G, int shift,
+                  int head_pattern, double rope_base, double pos_scale,
+                  void* workspace, size_t workspace_bytes, void* stream);
+int s2attn_bwd_ex(const void* q, const void* k, const void* v, const void* out,
+                  const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                  int B, int N, int H, int Hkv, int D, int G, int shift,
+                  int head_pattern, double rope_base, double pos_scale,
+                  void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static description of a status code. */
 const char* s2attn_strerror(int status);

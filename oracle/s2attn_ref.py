@@ -59,11 +59,26 @@ def _row_block(G: int) -> int:
 # Head split and the roll
 # ---------------------------------------------------------------------------
 
-def head_shift(h: int, H: int, shift: int) -> int:
-    """Shift applied to head ``h``: the second half of the heads (h >= H/2) is
-    shifted, the first half is not ([AIMech] opening definition; [Guide]
-    "1. Head Splitting into Standard and Shifted Groups")."""
-    return int(shift) if h >= H // 2 else 0
+HEAD_PATTERNS = ("second_half", "alternate")
+
+
+def head_shift(h: int, H: int, shift: int, pattern: str = "second_half", Hkv: int | None = None) -> int:
+    """Shift applied to head ``h``.
+
+    "second_half": the second half of the heads (h >= H/2) is shifted, the
+    first half is not ([AIMech] opening definition; [Guide] "1. Head
+    Splitting into Standard and Shifted Groups").
+    "alternate": alternate heads are shifted, heads 1, 3, 5, ... in the
+    illustration of [Concept] "Shifted sparse attention".  With grouped-query
+    sharing (Hkv < H) it is read as the q heads of the odd k/v heads, which
+    is the odd heads when Hkv = H.
+    """
+    if pattern == "second_half":
+        return int(shift) if h >= H // 2 else 0
+    if pattern == "alternate":
+        r = H // (Hkv if Hkv else H)
+        return int(shift) if (h // r) % 2 == 1 else 0
+    raise ValueError(f"unknown head pattern {pattern!r}")
 
 
 def kv_head(h: int, H: int, Hkv: int) -> int:
@@ -194,7 +209,7 @@ def group_causal_attention_backward(qg, kg, vg, dog, scale):
 # Whole S2-Attn forward and backward
 # ---------------------------------------------------------------------------
 
-def _check(q, k, G, shift):
+def _check(q, k, G, shift, head_pattern="second_half"):
     B, N, H, D = q.shape
     Hkv = k.shape[2]
     if G <= 0 or N % G != 0:
@@ -203,7 +218,7 @@ def _check(q, k, G, shift):
         raise ValueError("shift must lie in [0, G)")
     if H % Hkv != 0:
         raise ValueError("H must be a multiple of Hkv")
-    if shift > 0 and (H % 2 != 0 or Hkv % 2 != 0):
+    if head_pattern == "second_half" and shift > 0 and (H % 2 != 0 or Hkv % 2 != 0):
         raise ValueError("a shifted half needs an even number of q and k/v heads")
     return B, N, H, Hkv, D
 
@@ -216,7 +231,7 @@ def _rotated(q, k, rope):
     return rope_rotate(q, pos, base, s), rope_rotate(k, pos, base, s)
 
 
-def s2attn_forward(q, k, v, G, shift, rope=None):
+def s2attn_forward(q, k, v, G, shift, rope=None, head_pattern="second_half"):
     """S2-Attn forward on float64 arrays q [B,N,H,D], k/v [B,N,Hkv,D].
 
     Steps of the AIMech definition, in order: (optional RoPE at the original
@@ -224,7 +239,7 @@ def s2attn_forward(q, k, v, G, shift, rope=None):
     causal attention per group, reshape back, roll the shifted heads' output
     by +shift.  Returns (out [B,N,H,D], lse [B,H,N]).
     """
-    B, N, H, Hkv, D = _check(q, k, G, shift)
+    B, N, H, Hkv, D = _check(q, k, G, shift, head_pattern)
     qr, kr = _rotated(q, k, rope)
     scale = 1.0 / math.sqrt(D)
     NG = N // G
@@ -232,7 +247,7 @@ def s2attn_forward(q, k, v, G, shift, rope=None):
     lse = np.empty((B, H, N), dtype=np.float64)
     for b in range(B):
         for h in range(H):
-            sig = head_shift(h, H, shift)
+            sig = head_shift(h, H, shift, head_pattern, Hkv)
             kvh = kv_head(h, H, Hkv)
             qh = roll_sequence(qr[b, :, h, :], -sig).reshape(NG, G, D)
             kh = roll_sequence(kr[b, :, kvh, :], -sig).reshape(NG, G, D)
@@ -246,7 +261,7 @@ def s2attn_forward(q, k, v, G, shift, rope=None):
     return out, lse
 
 
-def s2attn_backward(q, k, v, dout, G, shift, rope=None):
+def s2attn_backward(q, k, v, dout, G, shift, rope=None, head_pattern="second_half"):
     """Gradients of ``s2attn_forward``'s output w.r.t. q, k, v for the upstream
     gradient ``dout`` [B,N,H,D].
 
@@ -256,7 +271,7 @@ def s2attn_backward(q, k, v, dout, G, shift, rope=None):
     summed, and with RoPE the gradients of q and k pass back through the
     transposed rotation.  Returns (dq, dk, dv) with the input shapes.
     """
-    B, N, H, Hkv, D = _check(q, k, G, shift)
+    B, N, H, Hkv, D = _check(q, k, G, shift, head_pattern)
     qr, kr = _rotated(q, k, rope)
     scale = 1.0 / math.sqrt(D)
     NG = N // G
@@ -265,7 +280,7 @@ def s2attn_backward(q, k, v, dout, G, shift, rope=None):
     dv = np.zeros((B, N, Hkv, D), dtype=np.float64)
     for b in range(B):
         for h in range(H):
-            sig = head_shift(h, H, shift)
+            sig = head_shift(h, H, shift, head_pattern, Hkv)
             kvh = kv_head(h, H, Hkv)
             qh = roll_sequence(qr[b, :, h, :], -sig).reshape(NG, G, D)
             kh = roll_sequence(kr[b, :, kvh, :], -sig).reshape(NG, G, D)
@@ -386,20 +401,20 @@ def dense_causal_attention(q, k, v):
     return out, lse
 
 
-def brute_force_masked_attention(q, k, v, G, shift):
+def brute_force_masked_attention(q, k, v, G, shift, head_pattern="second_half"):
     """S2-Attn as dense N x N attention under an explicit mask; no roll and no
     reshape.  Token p of a head with shift sigma sits at rolled index
     rho(p) = (p - sigma) mod N; p may attend to p' exactly when both fall in
     the same group (floor(rho/G) equal) and rho(p') <= rho(p).
     Returns (out [B,N,H,D], lse [B,H,N]).  For tiny N only.
     """
-    B, N, H, Hkv, D = _check(q, k, G, shift)
+    B, N, H, Hkv, D = _check(q, k, G, shift, head_pattern)
     c = 1.0 / math.sqrt(D)
     out = np.empty((B, N, H, D))
     lse = np.empty((B, H, N))
     for b in range(B):
         for h in range(H):
-            sig = head_shift(h, H, shift)
+            sig = head_shift(h, H, shift, head_pattern, Hkv)
             kvh = kv_head(h, H, Hkv)
             rho = (np.arange(N) - sig) % N
             grp = rho // G

@@ -160,3 +160,14 @@ def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(_lib, "LIB_PATH", "/nonexistent/libs2attn.so")
     with pytest.raises(RuntimeError, match="not built"):
         _lib.lib()
+
+
+def test_general_entry_points_check_the_head_pattern():
+    L = _lib.lib()
+    args = (FAKE, FAKE, FAKE, FAKE, FAKE, 1, 256, 4, 4, 64, 64, 32)
+    assert L.s2attn_fwd_ex(*args, 2, 0.0, 1.0, None, 0, None) == EINVAL
+    assert "head_pattern" in detail()
+    # Alternate heads need no even head count; an empty call validates only.
+    assert L.s2attn_fwd_ex(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 0, 3, 3, 64, 64, 32, 1, 0.0, 1.0, None, 0, None) == 0
+    assert L.s2attn_fwd_ex(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 0, 3, 3, 64, 64, 32, 0, 0.0, 1.0, None, 0, None) == EINVAL
+    assert L.s2attn_fwd_ex(*args, 1, -1.0, 1.0, FAKE, 1 << 20, None) == EINVAL  # bad RoPE base

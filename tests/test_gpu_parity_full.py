@@ -32,11 +32,17 @@ class Run:
         self.B, self.N, self.H, self.Hkv, self.D, self.G, self.sh = (
             c[k] for k in ("B", "N", "H", "Hkv", "D", "G", "shift"))
         self.rope = c["rope"]
+        self.pattern = c.get("head_pattern", "second_half")
         print(f"  generating {name}", flush=True)
         self.x = workloads.make_inputs(self.B, self.N, self.H, self.Hkv, self.D, seed=seed)
         q, k, v, do = (to_gpu(self.x[n]) for n in ("q", "k", "v", "dout"))
         print(f"  running {name} on the GPU", flush=True)
-        if self.rope is None:
+        if self.pattern != "second_half":
+            self.out, self.lse = ops.s2attn_fwd_ex(q, k, v, self.G, self.sh, head_pattern=self.pattern,
+                                                   rope=self.rope)
+            self.dq, self.dk, self.dv = ops.s2attn_bwd_ex(q, k, v, self.out, self.lse, do, self.G, self.sh,
+                                                          head_pattern=self.pattern, rope=self.rope)
+        elif self.rope is None:
             self.out, self.lse = ops.s2attn_fwd(q, k, v, self.G, self.sh)
             self.dq, self.dk, self.dv = ops.s2attn_bwd(q, k, v, self.out, self.lse, do, self.G, self.sh)
         else:
@@ -47,13 +53,16 @@ class Run:
         self.do = do
         self.NG = self.N // self.G
 
+    def shift_of(self, h):
+        return oracle.head_shift(h, self.H, self.sh, self.pattern, self.Hkv)
+
     def head(self, name, h):
         return workloads.f64_from_bf16_bits(self.x[name][0, :, h, :])
 
     def check_forward_unit(self, h, g):
         kvh = oracle.kv_head(h, self.H, self.Hkv)
         pos, o, l = oracle.head_unit_forward(self.head("q", h), self.head("k", kvh), self.head("v", kvh),
-                                             self.G, oracle.head_shift(h, self.H, self.sh), g, rope=self.rope)
+                                             self.G, self.shift_of(h), g, rope=self.rope)
         idx = torch.from_numpy(pos).cuda()
         assert_close(f"out[h{h},g{g}]", to_f64(self.out[0, :, h][idx]), o)
         assert_close(f"lse[h{h},g{g}]", to_f64(self.lse[0, h][idx]), l, max_abs=LSE_MAX_ABS, half_ulp_rel=0.0)
@@ -67,7 +76,7 @@ class Run:
         for h in heads:
             pos, uq, uk, uv = oracle.head_unit_backward(
                 self.head("q", h), self.head("k", kvh), self.head("v", kvh), self.head("dout", h),
-                self.G, oracle.head_shift(h, self.H, self.sh), g, rope=self.rope)
+                self.G, self.shift_of(h), g, rope=self.rope)
             dk = uk if dk is None else dk + uk
             dv = uv if dv is None else dv + uv
             if check_dq_heads is None or h in check_dq_heads:
@@ -82,7 +91,7 @@ class Run:
         r = self.H // self.Hkv
         worst_k = worst_v = 0.0
         for kvh in range(self.Hkv):
-            sh = oracle.head_shift(kvh * r, self.H, self.sh)
+            sh = self.shift_of(kvh * r)
             dk = self.dk[0, :, kvh].float()
             if self.rope is not None:
                 # Gradient w.r.t. the rotated keys: rotate the returned one.
@@ -208,3 +217,19 @@ def test_rope_base8_32k_forward_units(h, g):
 
 def test_rope_base8_32k_backward_unit():
     run_of("llama2_7b_n32k_rope_base8").check_backward_kv_group(20, 3)
+
+
+# ------------------------------------------------ alternate heads shifted
+
+@pytest.mark.parametrize("h,g", [(0, 3), (1, 0), (30, 1), (31, 3)])
+def test_alternate_32k_forward_units(h, g):
+    run_of("llama2_7b_n32k_alternate").check_forward_unit(h, g)
+
+
+@pytest.mark.parametrize("kvh,g", [(1, 3), (30, 0)])
+def test_alternate_32k_backward_units(kvh, g):
+    run_of("llama2_7b_n32k_alternate").check_backward_kv_group(kvh, g)
+
+
+def test_alternate_32k_gradient_invariants():
+    run_of("llama2_7b_n32k_alternate").check_gradient_invariants()

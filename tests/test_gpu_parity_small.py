@@ -220,3 +220,48 @@ def test_backward_stages_equal_the_composite_call():
     torch.cuda.synchronize()
     for a, b in ((dq, dq2), (dk, dk2), (dv, dv2)):
         assert np.array_equal(to_bits(a), to_bits(b))
+
+
+# Alternate-head shifting through the general entry points: without sharing
+# (odd H included, and the eight-wave kernel), with grouped-query sharing and
+# RoPE, and with one k/v head (no head is then shifted).
+ALT_CASES = [
+    ("alt_mha", 1, 512, 4, 4, 64, 128, 64, None),
+    ("alt_gqa_rope", 1, 1024, 8, 4, 128, 256, 128, (10000.0, 8.0)),
+    ("alt_odd_heads_large_tiles", 1, 4096, 3, 3, 128, 2048, 1024, None),
+    ("alt_mqa", 1, 512, 4, 1, 64, 128, 64, None),
+]
+
+
+@pytest.mark.parametrize("case", ALT_CASES, ids=[c[0] for c in ALT_CASES])
+def test_alternate_heads_match_oracle(case):
+    name, B, N, H, Hkv, D, G, sh, rope = case
+    x = workloads.make_inputs(B, N, H, Hkv, D, seed=1)
+    q, k, v, do = (to_gpu(x[n]) for n in ("q", "k", "v", "dout"))
+    out, lse = ops.s2attn_fwd_ex(q, k, v, G, sh, head_pattern="alternate", rope=rope)
+    dq, dk, dv = ops.s2attn_bwd_ex(q, k, v, out, lse, do, G, sh, head_pattern="alternate", rope=rope)
+    torch.cuda.synchronize()
+    x64 = {n: workloads.f64_from_bf16_bits(a) for n, a in x.items()}
+    ref_o, ref_l = oracle.s2attn_forward(x64["q"], x64["k"], x64["v"], G, sh, rope=rope, head_pattern="alternate")
+    assert_close("out", to_f64(out), ref_o)
+    assert_close("lse", to_f64(lse), ref_l, max_abs=LSE_MAX_ABS, half_ulp_rel=0.0)
+    rq, rk, rv = oracle.s2attn_backward(x64["q"], x64["k"], x64["v"], x64["dout"], G, sh, rope=rope,
+                                        head_pattern="alternate")
+    assert_close("dq", to_f64(dq), rq)
+    assert_close("dk", to_f64(dk), rk, max_abs=kv_grad_max_abs(H, Hkv))
+    assert_close("dv", to_f64(dv), rv, max_abs=kv_grad_max_abs(H, Hkv))
+
+
+def test_general_entry_points_match_the_specific_ones():
+    # Second-half pattern through s2attn_fwd_ex / s2attn_bwd_ex equals
+    # s2attn_fwd / s2attn_bwd bit for bit (same kernels, same arguments).
+    B, N, H, Hkv, D, G, sh = 1, 512, 4, 2, 128, 128, 64
+    x = workloads.make_inputs(B, N, H, Hkv, D, seed=2)
+    q, k, v, do = (to_gpu(x[n]) for n in ("q", "k", "v", "dout"))
+    out, lse = ops.s2attn_fwd(q, k, v, G, sh)
+    dq, dk, dv = ops.s2attn_bwd(q, k, v, out, lse, do, G, sh)
+    out2, lse2 = ops.s2attn_fwd_ex(q, k, v, G, sh)
+    dq2, dk2, dv2 = ops.s2attn_bwd_ex(q, k, v, out2, lse2, do, G, sh)
+    for a, b in ((out, out2), (dq, dq2), (dk, dk2), (dv, dv2)):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.equal(lse, lse2)

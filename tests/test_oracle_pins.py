@@ -412,3 +412,64 @@ def test_pins_catch_a_reversed_rotation(monkeypatch):
     _planted(monkeypatch, "rope_angles", lambda p, D, b, s: -orig(p, D, b, s))
     with pytest.raises(AssertionError):
         test_rope_direction_and_angle_closed_form()
+
+
+# ---------------------------------------------------------------------------
+# Alternate-head shifting ("LoRA for Long-Context Adaptation", section
+# "Shifted sparse attention": heads 1, 3, 5, ... shifted)
+# ---------------------------------------------------------------------------
+
+def test_alternate_pattern_shifts_the_odd_heads():
+    assert [ref.head_shift(h, 4, 32, "alternate") for h in range(4)] == [0, 32, 0, 32]
+    # Grouped-query sharing: the q heads of the odd k/v heads (two q heads each).
+    assert [ref.head_shift(h, 8, 8, "alternate", 4) for h in range(8)] == [0, 0, 8, 8, 0, 0, 8, 8]
+    with pytest.raises(ValueError):
+        ref.head_shift(0, 4, 32, "every_third")
+
+
+def test_alternate_pattern_worked_example():
+    # The page's illustration: G = 2048, heads 1, 3, 5, ... shifted by 1024
+    # cover tokens 1024 ... 3071 in their first group; heads 0, 2, 4 cover
+    # 0 ... 2047.
+    N, G = 8192, 2048
+    for h in (1, 3, 5):
+        pos = ref.unit_positions(N, G, ref.head_shift(h, 8, G // 2, "alternate"), 0)
+        assert np.array_equal(pos, np.arange(1024, 3072))
+    for h in (0, 2, 4):
+        pos = ref.unit_positions(N, G, ref.head_shift(h, 8, G // 2, "alternate"), 0)
+        assert np.array_equal(pos, np.arange(0, 2048))
+
+
+def _half_order(H, Hkv):
+    """q and k/v head orders that move the alternate pattern's shifted heads
+    (the odd k/v heads and their q heads) into the second half."""
+    r = H // Hkv
+    kv = [j for j in range(Hkv) if j % 2 == 0] + [j for j in range(Hkv) if j % 2 == 1]
+    qh = [j * r + i for j in kv for i in range(r)]
+    return np.array(qh), np.array(kv)
+
+
+@pytest.mark.parametrize("N,G,shift,H,Hkv,D", [(32, 8, 4, 4, 4, 8), (32, 8, 4, 8, 4, 8), (24, 6, 3, 4, 2, 4)])
+def test_alternate_pattern_is_the_half_pattern_on_reordered_heads(N, G, shift, H, Hkv, D):
+    # Heads are independent, so shifting the odd heads equals shifting the
+    # second half after reordering the heads so the odd ones come last.
+    q, k, v, do = _qkv(1, N, H, Hkv, D, seed=11 + H + Hkv)
+    qo, ko = _half_order(H, Hkv)
+    out_a, lse_a = oracle.s2attn_forward(q, k, v, G, shift, head_pattern="alternate")
+    out_h, lse_h = oracle.s2attn_forward(q[:, :, qo], k[:, :, ko], v[:, :, ko], G, shift)
+    assert np.max(np.abs(out_a[:, :, qo] - out_h)) < 1e-12
+    assert np.max(np.abs(lse_a[:, qo] - lse_h)) < 1e-12
+    dq_a, dk_a, dv_a = oracle.s2attn_backward(q, k, v, do, G, shift, head_pattern="alternate")
+    dq_h, dk_h, dv_h = oracle.s2attn_backward(q[:, :, qo], k[:, :, ko], v[:, :, ko], do[:, :, qo], G, shift)
+    assert np.max(np.abs(dq_a[:, :, qo] - dq_h)) < 1e-12
+    assert np.max(np.abs(dk_a[:, :, ko] - dk_h)) < 1e-12
+    assert np.max(np.abs(dv_a[:, :, ko] - dv_h)) < 1e-12
+
+
+@pytest.mark.parametrize("N,G,shift,H,Hkv,D", [(16, 8, 4, 4, 4, 8), (24, 6, 5, 6, 2, 4), (16, 8, 4, 3, 3, 8)])
+def test_alternate_pattern_brute_force_mask_agrees(N, G, shift, H, Hkv, D):
+    q, k, v, _ = _qkv(1, N, H, Hkv, D, seed=3 * N + G)
+    out, lse = oracle.s2attn_forward(q, k, v, G, shift, head_pattern="alternate")
+    o_bf, l_bf = ref.brute_force_masked_attention(q, k, v, G, shift, head_pattern="alternate")
+    assert np.max(np.abs(out - o_bf)) < 1e-12
+    assert np.max(np.abs(lse - l_bf)) < 1e-12

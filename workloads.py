@@ -35,6 +35,10 @@ WORKLOADS = {
                                       rope=(10000.0, 25.0)),
     "llama2_7b_n32k_rope_base8": dict(B=1, N=32768, H=32, Hkv=32, D=128, G=8192, shift=4096,
                                       rope=(80000.0, 1.0)),
+    # Alternate heads shifted instead of the second half (the variant of the
+    # "LoRA for Long-Context Adaptation" page).
+    "llama2_7b_n32k_alternate": dict(B=1, N=32768, H=32, Hkv=32, D=128, G=8192, shift=4096, rope=None,
+                                     head_pattern="alternate"),
 }
 
 # The workload the benchmark times: LLaMA2-7B attention at 32k context.
