@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for Shifted Sparse Attention (S2-Attn).
+"""fp64 CPU oracle for Shifted Sparse Attention (S2-Attn) and for the
+LoRA-adapted q/k/v projections ahead of it.
 
 TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
 link this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
@@ -28,4 +29,9 @@ from .s2attn_ref import (  # noqa: F401
     unit_positions,
     dense_causal_attention,
     brute_force_masked_attention,
+)
+from .lora_qkv_ref import (  # noqa: F401
+    lora_projection,
+    lora_qkv_forward,
+    lora_qkv_backward,
 )

@@ -92,3 +92,42 @@ def make_inputs_f32(B, N, H, Hkv, D, seed=0):
     rng = np.random.default_rng(seed)
     return {name: rng.standard_normal((B, N, heads, D), dtype=np.float32)
             for name, heads in (("q", H), ("k", Hkv), ("v", Hkv))}
+
+
+# LoRA-adapted q/k/v projections ahead of the attention path.  M = B * N
+# token rows of the model width d_in; q has H * D output columns, k and v
+# Hkv * D each; rank r within the 64-128 the "LoRA for Long-Context
+# Adaptation" page recommends for long-context extension.
+LORA_WORKLOADS = {
+    "lora_qkv_tiny": dict(M=300, d_in=192, widths=(256, 128, 128), r=16, scale=1.0),
+    "lora_qkv_llama2_7b_n32k": dict(M=32768, d_in=4096, widths=(4096, 4096, 4096), r=64, scale=1.0),
+    "lora_qkv_llama2_70b_gqa_n32k": dict(M=32768, d_in=8192, widths=(8192, 1024, 1024), r=64, scale=1.0),
+}
+
+LORA_BENCH_WORKLOAD = "lora_qkv_llama2_7b_n32k"
+
+
+def make_lora_inputs(M, d_in, widths, r, seed=0, with_dy=False):
+    """Seeded bfloat16 inputs for the LoRA q/k/v projections (uint16 bits).
+
+    Storage orientation (the one the library takes): x [M, d_in]; for each
+    target p in (q, k, v): wt[p] [width_p, d_in] (the frozen weight, one row
+    per output column), at[p] [r, d_in] (A transposed), bt[p] [width_p, r]
+    (B transposed); dy[p] [M, width_p] when ``with_dy``.  Draw order: x, the
+    three wt, the three at, the three bt, then the three dy, each
+    ``standard_normal(float32)`` scaled before rounding: x and dy by 1,
+    wt and at by 1/sqrt(d_in), bt by 1/sqrt(r), so every output column has
+    unit-order magnitude (hidden states after RMSNorm, a trained adapter).
+    """
+    rng = np.random.default_rng(seed)
+
+    def draw(shape, s):
+        return bf16_bits_from_f32(rng.standard_normal(shape, dtype=np.float32) * np.float32(s))
+
+    out = {"x": draw((M, d_in), 1.0)}
+    out["wt"] = [draw((w, d_in), 1.0 / np.sqrt(d_in)) for w in widths]
+    out["at"] = [draw((r, d_in), 1.0 / np.sqrt(d_in)) for _ in widths]
+    out["bt"] = [draw((w, r), 1.0 / np.sqrt(max(r, 1))) for w in widths]
+    if with_dy:
+        out["dy"] = [draw((M, w), 1.0) for w in widths]
+    return out
