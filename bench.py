@@ -19,7 +19,9 @@ Prints ONE JSON line.  Options:
   --warmup W      untimed steps first (default 5)
   --workload W    a key of workloads.WORKLOADS (with RoPE or alternate-head
                   shifting: the general entry points are timed as two calls,
-                  forward and backward)
+                  forward and backward), or of workloads.LORA_WORKLOADS: the
+                  LoRA q/k/v projections ahead of the attention, one call
+                  per step, with the library GEMM timed beside for context
   --no-cpu-baseline   skip timing the fp64 oracle on a sample
   --calib-copy-mib M  also run one plain device copy of M MiB (for counter calibration)
 """
@@ -94,6 +96,140 @@ def cpu_baseline(cfg, x_bits, budget_s=20.0):
     }
 
 
+LORA_METRIC = "LoRA q/k/v projection TFLOP/s and % bf16 MFMA peak"
+
+
+def lora_flops(M, d_in, widths, r):
+    """MFMA work of one projection call: the frozen products, x A and (x A) B."""
+    wsum = sum(widths)
+    return 2.0 * M * d_in * wsum + 2.0 * M * d_in * 3 * r + 2.0 * M * r * wsum
+
+
+def lora_cpu_baseline(cfg, d, budget_s):
+    """The fp64 oracle on a bounded sample of token rows of the same inputs."""
+    import numpy as np
+
+    import oracle
+    from workloads import f64_from_bf16_bits
+    M, d_in, widths, r, s = cfg["M"], cfg["d_in"], cfg["widths"], cfg["r"], cfg["scale"]
+    Ws = [f64_from_bf16_bits(w).T for w in d["wt"]]
+    ads = [(f64_from_bf16_bits(a).T, f64_from_bf16_bits(b).T) for a, b in zip(d["at"], d["bt"])]
+    rows, done = 256, 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s and done < M:
+        x = f64_from_bf16_bits(d["x"][done:done + rows])
+        oracle.lora_qkv_forward(x, Ws, ads, s)
+        done += x.shape[0]
+    dt = time.perf_counter() - t0
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [(i.get("internal_api"), i.get("num_threads")) for i in threadpool_info()]
+    except Exception:
+        blas = []
+    return {
+        "value": lora_flops(done, d_in, widths, r) / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": max([n for _, n in blas if n] or [1]),
+        "kind": "oracle",
+        "sample": f"the first {done} of {M} token rows of {cfg['name']} (all three projections), float64 "
+                  f"NumPy, {dt:.1f} s; rows do identical work, so the rate is the whole workload's",
+        "host_cpus": len(os.sched_getaffinity(0)),
+        "blas": blas,
+        "seconds": dt,
+    }
+
+
+def bench_lora(args, name):
+    import numpy as np
+    import torch
+    import torch.nn.functional as F
+
+    import workloads
+    from grouped_shifted_attention_amd import ops
+    cfg = dict(workloads.LORA_WORKLOADS[name], name=name)
+    M, d_in, widths, r, s = cfg["M"], cfg["d_in"], cfg["widths"], cfg["r"], cfg["scale"]
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d = workloads.make_lora_inputs(M, d_in, widths, r, seed=0)
+    to_gpu = lambda bits: torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    x = to_gpu(d["x"])
+    wt = [to_gpu(w) for w in d["wt"]]
+    at = [to_gpu(a) for a in d["at"]]
+    bt = [to_gpu(b) for b in d["bt"]]
+    outs = tuple(torch.empty(M, w, dtype=torch.bfloat16, device=dev) for w in widths)
+    ws = ops.lora_qkv_workspace(M, r, dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        ops.s2attn_lora_qkv_fwd(x, wt, at, bt, s, out=outs, workspace=ws)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / max(args.steps, 1)
+    call_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    fl = lora_flops(M, d_in, widths, r)
+    value = fl / (ms_step * 1e-3) / 1e12
+    achieved = fl / (call_ms * 1e-3) / 1e12
+
+    # Context: the library GEMM (hipBLASLt through torch) for the frozen part
+    # alone, all three weights concatenated into one [sum(widths), d_in].
+    wcat = torch.cat(wt, 0).contiguous()
+    for _ in range(3):
+        F.linear(x, wcat)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(10):
+        F.linear(x, wcat)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    lib_ms = e0.elapsed_time(e1) / 10
+    lib_tf = 2.0 * M * d_in * sum(widths) / (lib_ms * 1e-3) / 1e12
+    alg_bytes = 2.0 * (M * d_in + sum(widths) * d_in + M * sum(widths) + 3 * r * d_in + sum(widths) * r
+                       + 2 * M * 3 * r)
+    line = {
+        "metric": LORA_METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": name, "M": M, "d_in": d_in, "widths": list(widths), "r": r, "scale": s,
+                   "parallelism": "single-gpu"},
+        "pct_peak": 100.0 * value / PEAK_BF16_TFLOPS,
+        "kernel_ms": {"lora_qkv_call": call_ms},
+        "roofline": {"bound": "mfma", "kernel": "lora_qkv_call", "achieved": achieved,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": None, "avg_launch_ms": call_ms},
+        "hbm_gbs_algorithmic": {"call": alg_bytes / (call_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS},
+        "library_frozen_gemm": {"what": "torch F.linear (hipBLASLt) of x by the three frozen weights "
+                                        "concatenated, no adapter", "ms": lib_ms, "tflops": lib_tf},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = lora_cpu_baseline(cfg, d, args.cpu_budget_s)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -118,6 +254,8 @@ def main():
     from grouped_shifted_attention_amd import flops, ops
 
     name = args.workload or workloads.BENCH_WORKLOAD
+    if name in workloads.LORA_WORKLOADS:
+        return bench_lora(args, name)
     cfg = dict(workloads.WORKLOADS[name], name=name)
     rope = cfg["rope"]
     pattern = cfg.get("head_pattern", "second_half")

@@ -22,4 +22,6 @@ from .ops import (  # noqa: F401
     s2attn_fwd,
     s2attn_fwd_rope,
     s2attn_workspace_sizes,
+    s2attn_lora_qkv_fwd,
+    lora_qkv_workspace,
 )

@@ -10,6 +10,7 @@
 #include <string>
 
 #include "kernels.hpp"
+#include "lora_kernels.hpp"
 
 namespace {
 
@@ -359,6 +360,73 @@ int s2attn_bwd_ex(const void* q, const void* k, const void* v, const void* out, 
   return guarded([&] {
     return do_bwd(q, k, v, out, lse, dout, dq, dk, dv, B, N, H, Hkv, D, G, shift,
                   rope_base != 0.0 ? rope : nullptr, workspace, workspace_bytes, stream, head_pattern);
+  });
+}
+
+size_t s2attn_lora_qkv_workspace_size(int M, int r) {
+  if (M <= 0 || r <= 0) return 0;
+  return round_up((size_t)M * 3 * r * 2);
+}
+
+int s2attn_lora_qkv_fwd(const void* x, int M, int d_in, const void* wq_t, const void* wk_t, const void* wv_t,
+                        int width_q, int width_kv, const void* aq_t, const void* ak_t, const void* av_t,
+                        const void* bq_t, const void* bk_t, const void* bv_t, int r, double scale, void* q,
+                        void* k, void* v, void* workspace, size_t workspace_bytes, void* stream) {
+  return guarded([&] {
+    if (M < 0) return fail(S2ATTN_EINVAL, "M must be >= 0");
+    if (d_in < 64 || d_in % 64 != 0 || d_in > (1 << 20))
+      return fail(S2ATTN_EINVAL, "d_in must be a multiple of 64 in [64, 2^20]");
+    if (width_q < 64 || width_q % 64 != 0 || width_kv < 64 || width_kv % 64 != 0)
+      return fail(S2ATTN_EINVAL, "width_q and width_kv must be multiples of 64 (>= 64)");
+    if (r < 0 || r > 1024 || r % 8 != 0) return fail(S2ATTN_EINVAL, "r must be 0 or a multiple of 8 up to 1024");
+    if (!std::isfinite(scale)) return fail(S2ATTN_EINVAL, "scale must be finite");
+    const double tiles = std::ceil(M / 256.0) *
+                         (double)(s2a::lora_col_tiles(width_q) + 2 * s2a::lora_col_tiles(width_kv));
+    if (tiles > 2147483647.0) return fail(S2ATTN_EINVAL, "too many work items for one launch");
+    if (M == 0) return (int)S2ATTN_OK;
+    const size_t xb = (size_t)M * d_in * 2;
+    const size_t wqb = (size_t)width_q * d_in * 2, wkb = (size_t)width_kv * d_in * 2;
+    const size_t ab = (size_t)r * d_in * 2, bqb = (size_t)width_q * r * 2, bkb = (size_t)width_kv * r * 2;
+    const size_t yqb = (size_t)M * width_q * 2, ykb = (size_t)M * width_kv * 2;
+    const size_t need = s2attn_lora_qkv_workspace_size(M, r);
+    if (r > 0) {
+      if (workspace == nullptr) return fail(S2ATTN_EINVAL, "workspace is NULL");
+      if (workspace_bytes < need)
+        return fail(S2ATTN_EINVAL, "workspace too small: need " + std::to_string(need) + " bytes");
+      if (((uintptr_t)workspace & (kAlign - 1)) != 0) return fail(S2ATTN_EINVAL, "workspace is not 256-byte aligned");
+      const Buf in[] = {{x, xb, "x"},     {wq_t, wqb, "wq_t"}, {wk_t, wkb, "wk_t"}, {wv_t, wkb, "wv_t"},
+                        {aq_t, ab, "aq_t"}, {ak_t, ab, "ak_t"},  {av_t, ab, "av_t"},  {bq_t, bqb, "bq_t"},
+                        {bk_t, bkb, "bk_t"}, {bv_t, bkb, "bv_t"}};
+      const Buf out[] = {{q, yqb, "q"}, {k, ykb, "k"}, {v, ykb, "v"}, {workspace, need, "workspace"}};
+      int st = check_buffers(in, 10, out, 4);
+      if (st) return st;
+    } else {
+      const Buf in[] = {{x, xb, "x"}, {wq_t, wqb, "wq_t"}, {wk_t, wkb, "wk_t"}, {wv_t, wkb, "wv_t"}};
+      const Buf out[] = {{q, yqb, "q"}, {k, ykb, "k"}, {v, ykb, "v"}};
+      int st = check_buffers(in, 4, out, 3);
+      if (st) return st;
+    }
+    s2a::LoraQkvArgs a{};
+    a.x = (const uint16_t*)x;
+    a.M = M;
+    a.K = d_in;
+    const void* wt[3] = {wq_t, wk_t, wv_t};
+    const void* at[3] = {aq_t, ak_t, av_t};
+    const void* bt[3] = {bq_t, bk_t, bv_t};
+    void* y[3] = {q, k, v};
+    for (int p = 0; p < 3; ++p) {
+      a.wt[p] = (const uint16_t*)wt[p];
+      a.at[p] = r > 0 ? (const uint16_t*)at[p] : nullptr;
+      a.bt[p] = r > 0 ? (const uint16_t*)bt[p] : nullptr;
+      a.width[p] = p == 0 ? width_q : width_kv;
+      a.y[p] = (uint16_t*)y[p];
+    }
+    a.r = r;
+    a.scale = (float)scale;
+    a.t = r > 0 ? (uint16_t*)workspace : nullptr;
+    hipError_t e = s2a::launch_lora_qkv(a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "lora_qkv launch");
+    return (int)S2ATTN_OK;
   });
 }
 

@@ -249,6 +249,56 @@ def s2attn_workspace_sizes(B, N, H, Hkv, D):
     }
 
 
+def lora_qkv_workspace(M, r, device):
+    """A workspace tensor large enough for s2attn_lora_qkv_fwd (None when r = 0)."""
+    n = lib().s2attn_lora_qkv_workspace_size(int(M), int(r))
+    return None if n == 0 else _workspace(n, device)
+
+
+def s2attn_lora_qkv_fwd(x, wt, at=None, bt=None, scale=1.0, out=None, workspace=None):
+    """LoRA-adapted q/k/v projections: y_p = x W_p + scale (x A_p) B_p.
+
+    x [M, d_in]; wt = (wq_t, wk_t, wv_t) with wq_t [width_q, d_in] and wk_t,
+    wv_t [width_kv, d_in]; at = three [r, d_in] (A transposed) and bt =
+    (bq_t [width_q, r], bk_t, bv_t [width_kv, r]) (B transposed), or both None
+    for plain projections.  All bf16, contiguous, on one GPU.  Returns
+    (q, k, v, workspace): q [M, width_q], k, v [M, width_kv] and the workspace,
+    which then holds scale * x A_p for the three targets ([M, 3r] bf16).
+    """
+    if x.dim() != 2 or len(wt) != 3:
+        raise ValueError("x must be [M, d_in] and wt three weights")
+    M, d_in = x.shape
+    dev = x.device
+    _need(x, "x", torch.bfloat16, (M, d_in), None)
+    wq = wt[0].shape[0]
+    wkv = wt[1].shape[0]
+    for name, t, w in (("wq_t", wt[0], wq), ("wk_t", wt[1], wkv), ("wv_t", wt[2], wkv)):
+        _need(t, name, torch.bfloat16, (w, d_in), dev)
+    if (at is None) != (bt is None):
+        raise ValueError("at and bt must both be given or both be None")
+    r = 0 if at is None else at[0].shape[0]
+    if at is not None:
+        for p, (a, b) in enumerate(zip(at, bt)):
+            _need(a, f"at[{p}]", torch.bfloat16, (r, d_in), dev)
+            _need(b, f"bt[{p}]", torch.bfloat16, (wq if p == 0 else wkv, r), dev)
+    if out is None:
+        out = (torch.empty(M, wq, dtype=torch.bfloat16, device=dev),
+               torch.empty(M, wkv, dtype=torch.bfloat16, device=dev),
+               torch.empty(M, wkv, dtype=torch.bfloat16, device=dev))
+    for name, t, w in (("q", out[0], wq), ("k", out[1], wkv), ("v", out[2], wkv)):
+        _need(t, name, torch.bfloat16, (M, w), dev)
+    ws = lora_qkv_workspace(M, r, dev) if workspace is None else workspace
+    none3 = (None, None, None)
+    a3 = none3 if at is None else at
+    b3 = none3 if bt is None else bt
+    check(lib().s2attn_lora_qkv_fwd(
+        _ptr(x), M, d_in, _ptr(wt[0]), _ptr(wt[1]), _ptr(wt[2]), wq, wkv,
+        _ptr(a3[0]), _ptr(a3[1]), _ptr(a3[2]), _ptr(b3[0]), _ptr(b3[1]), _ptr(b3[2]), r, float(scale),
+        _ptr(out[0]), _ptr(out[1]), _ptr(out[2]), _ptr(ws),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(x)))
+    return out[0], out[1], out[2], ws
+
+
 class S2AttnFunction(torch.autograd.Function):
     """Autograd wrapper: forward saves q, k, v, out and lse; backward calls the
     library's backward entry point."""

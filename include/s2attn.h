@@ -176,6 +176,44 @@ int s2attn_bwd_ex(const void* q, const void* k, const void* v, const void* out,
                   int head_pattern, double rope_base, double pos_scale,
                   void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * LoRA-adapted q/k/v projections, the step ahead of the attention ("LoRA for
+ * Long-Context Adaptation", section "Why vanilla LoRA under-delivers on long
+ * context": two small trained matrices A (d x r) and B (r x d) added to each
+ * frozen target projection; "Practical recipe": the attention projections
+ * are the targets).  The formula itself is lost from the page; the reading
+ * implemented is, for each target p in (q, k, v) and token rows x,
+ *     y_p = x W_p + scale * (x A_p) B_p.
+ *
+ * Layouts (bf16, row-major, contiguous, 16-byte aligned):
+ *   x            [M, d_in]          token rows (M = B * N)
+ *   wq_t         [width_q, d_in]    W_q transposed: one row per output column
+ *   wk_t, wv_t   [width_kv, d_in]
+ *   aq_t ...     [r, d_in]          A_p transposed
+ *   bq_t         [width_q, r]       B_p transposed; bk_t, bv_t [width_kv, r]
+ *   q            [M, width_q]       = [B, N, H, D] with width_q = H * D
+ *   k, v         [M, width_kv]      = [B, N, Hkv, D] with width_kv = Hkv * D
+ * This is the weight[out][in] orientation of a linear layer.
+ *
+ * Limits: d_in, width_q and width_kv multiples of 64 (>= 64, d_in <= 2^20);
+ * r = 0 (no adapter: plain projections; the A, B pointers and the
+ * workspace may then be NULL) or a multiple of 8 up to 1024; scale finite.
+ * The workspace (s2attn_lora_qkv_workspace_size() bytes, 256-byte aligned)
+ * holds, after the call, scale * x A_p for the three targets side by side
+ * ([M, 3r] bf16): the low-rank activations a backward pass needs.  Products
+ * accumulate in float32; that intermediate and the outputs are rounded to
+ * bf16 once.  Outputs must not overlap any input or each other.
+ */
+size_t s2attn_lora_qkv_workspace_size(int M, int r);
+int s2attn_lora_qkv_fwd(const void* x, int M, int d_in,
+                        const void* wq_t, const void* wk_t, const void* wv_t,
+                        int width_q, int width_kv,
+                        const void* aq_t, const void* ak_t, const void* av_t,
+                        const void* bq_t, const void* bk_t, const void* bv_t,
+                        int r, double scale,
+                        void* q, void* k, void* v,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* s2attn_strerror(int status);
 

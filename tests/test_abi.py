@@ -171,3 +171,54 @@ def test_general_entry_points_check_the_head_pattern():
     assert L.s2attn_fwd_ex(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 0, 3, 3, 64, 64, 32, 1, 0.0, 1.0, None, 0, None) == 0
     assert L.s2attn_fwd_ex(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 0, 3, 3, 64, 64, 32, 0, 0.0, 1.0, None, 0, None) == EINVAL
     assert L.s2attn_fwd_ex(*args, 1, -1.0, 1.0, FAKE, 1 << 20, None) == EINVAL  # bad RoPE base
+
+
+# ------------------------------------------------- LoRA q/k/v projections
+
+def _lora(M=512, d_in=128, wq=256, wkv=128, r=16, scale=1.0, ws=True, ws_bytes=None, **ptrs):
+    L = _lib.lib()
+    need = L.s2attn_lora_qkv_workspace_size(M, r)
+    p = {n: FAKE + i * (1 << 28) for i, n in enumerate(
+        ("x", "wq", "wk", "wv", "aq", "ak", "av", "bq", "bk", "bv", "q", "k", "v", "ws"))}
+    p.update(ptrs)
+    return L.s2attn_lora_qkv_fwd(p["x"], M, d_in, p["wq"], p["wk"], p["wv"], wq, wkv,
+                                 p["aq"], p["ak"], p["av"], p["bq"], p["bk"], p["bv"], r, scale,
+                                 p["q"], p["k"], p["v"], p["ws"] if ws else None,
+                                 need if ws_bytes is None else ws_bytes, None)
+
+
+def test_lora_workspace_size():
+    L = _lib.lib()
+    assert L.s2attn_lora_qkv_workspace_size(1000, 64) == 1000 * 3 * 64 * 2  # already a multiple of 256
+    assert L.s2attn_lora_qkv_workspace_size(3, 8) == 256
+    assert L.s2attn_lora_qkv_workspace_size(1000, 0) == 0
+    assert L.s2attn_lora_qkv_workspace_size(0, 64) == 0
+
+
+@pytest.mark.parametrize("kw", [
+    dict(M=-1), dict(d_in=96), dict(d_in=0), dict(wq=100), dict(wkv=32), dict(r=12), dict(r=2048),
+    dict(r=-8), dict(scale=float("nan")), dict(scale=float("inf")),
+])
+def test_lora_rejects_bad_shapes(kw):
+    assert _lora(**kw) == EINVAL
+
+
+def test_lora_rejects_bad_buffers():
+    assert _lora(x=None) == EINVAL
+    assert _lora(bq=None) == EINVAL
+    assert _lora(q=FAKE + 8) == EINVAL                      # not 16-byte aligned
+    assert _lora(ws=False) == EINVAL                         # r > 0 needs the workspace
+    assert _lora(ws_bytes=100) == EINVAL
+    assert _lora(q=FAKE) == EINVAL                          # output overlaps x
+    assert _lora(k=FAKE + 10 * (1 << 28)) == EINVAL         # k overlaps q
+    assert b"overlaps" in _lib.lib().s2attn_last_error()
+
+
+def test_lora_empty_call_is_a_no_op():
+    assert _lora(M=0) == _lib.S2ATTN_OK
+
+
+def test_lora_without_adapter_needs_no_workspace():
+    # r = 0 with NULL adapters and workspace passes validation; M = 0 keeps it
+    # from launching.
+    assert _lora(M=0, r=0, aq=None, ak=None, av=None, bq=None, bk=None, bv=None, ws=False) == _lib.S2ATTN_OK
