@@ -96,6 +96,18 @@ def cpu_baseline(cfg, x_bits, budget_s=20.0):
     }
 
 
+def calib_copy(args, dev):
+    """One plain device copy of --calib-copy-mib MiB (counter calibration)."""
+    import torch
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+
 LORA_METRIC = "LoRA q/k/v projection TFLOP/s and % bf16 MFMA peak"
 
 
@@ -160,6 +172,7 @@ def bench_lora(args, name):
     bt = [to_gpu(b) for b in d["bt"]]
     outs = tuple(torch.empty(M, w, dtype=torch.bfloat16, device=dev) for w in widths)
     ws = ops.lora_qkv_workspace(M, r, dev)
+    calib_copy(args, dev)
     stream = torch.cuda.current_stream(dev)
 
     def step(ev=None):
@@ -276,13 +289,7 @@ def main():
     ws_f = ops.fwd_rope_workspace(q, k) if rope is not None else None
     stream = torch.cuda.current_stream(dev)
 
-    if args.calib_copy_mib > 0:
-        n = args.calib_copy_mib << 20
-        src = torch.ones(n, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    calib_copy(args, dev)
 
     kernels = ["fwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq"]
     if fused:
