@@ -337,11 +337,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 2
 // so each SIMD's matrix core works while its other wave is busy on the
 // vector ALU, instead of both waves waiting on the same unit at once.
 // X stages the K tiles and Y the V tiles through VGPRs: tile m+1 is loaded
-// at the start of the wave's matrix phase m and written to LDS at the end of
-// its softmax phase m.  Tile n sits in buffer n & 1.  K(m+1) (written in slot
-// 2m+1) replaces K(m-1), last read in slot 2m-1; V(m+1) (slot 2m+2) replaces
-// V(m-1), last read in slot 2m+1; each is first read two slots after its
-// write, past the barrier that ends the write slot.
+// at the start of the wave's matrix phase m and written to LDS at the start
+// of its softmax phase m (the writes then drain under the VALU work).  Tile n
+// sits in buffer n & 1.  K(m+1) (written in slot 2m+1) replaces K(m-1), last
+// read in slot 2m-1; V(m+1) (slot 2m+2) replaces V(m-1), last read in slot
+// 2m+1; each is first read two slots after its write, past the barrier that
+// ends the write slot.
 template <int D, bool ROPE>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_pp_kernel(FwdArgs a, RopeTable rope) {
   constexpr int BM = 256;
@@ -451,7 +452,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
   };
-  bf16x8 vpre[D / 32];  // first V^T fragments of the next PV, read at the end of the softmax phase
+  bf16x8 vpre[D / 32];  // first V^T fragments of the next PV, read at the start of the softmax phase
   auto mat_pv = [&](const uint16_t* vt) __attribute__((always_inline)) {
     constexpr int KS = kBN / 16;
     bf16x8 vf[2][D / 32];
@@ -585,10 +586,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (m < T) mat_s(kbuf(c));
     if (m < T) slot_barrier();
     if (m < T) {
-      softmax(m);
+      // The staged tile and the first V(m) fragments go to LDS first, so
+      // they drain during the VALU work instead of holding up the barrier.
+      // The target buffer held tile m-1, whose last reader (the other
+      // group's matrix phase) ended at the previous slot boundary.
       if (m + 1 < T) swrite(grp ? vbuf(Cn{}) : kbuf(Cn{}));
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) vpre[db] = vfrag(vbuf(c), db);  // V(m): visible since its write slot ended
+      softmax(m);
       if (grp == 0 || m + 1 < T) slot_barrier();
     }
   };
