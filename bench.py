@@ -108,7 +108,7 @@ def calib_copy(args, dev):
         del src, dst
 
 
-LORA_METRIC = "LoRA q/k/v projection TFLOP/s and % bf16 MFMA peak"
+LORA_METRIC = "LoRA q/k/v projection fwd+bwd TFLOP/s and % bf16 MFMA peak"
 
 
 def lora_flops(M, d_in, widths, r):
@@ -117,8 +117,16 @@ def lora_flops(M, d_in, widths, r):
     return 2.0 * M * d_in * wsum + 2.0 * M * d_in * 3 * r + 2.0 * M * r * wsum
 
 
-def lora_cpu_baseline(cfg, d, budget_s):
-    """The fp64 oracle on a bounded sample of token rows of the same inputs."""
+def lora_bwd_flops(M, d_in, widths, r):
+    """MFMA work of the backward: dy B^T, dx (frozen and low-rank parts), dA, dB."""
+    wsum = sum(widths)
+    return 2.0 * M * r * wsum + 2.0 * M * d_in * (wsum + 3 * r) + 2.0 * M * 3 * r * d_in + 2.0 * M * wsum * r
+
+
+def lora_cpu_baseline(cfg, d, dy_bits, budget_s):
+    """The fp64 oracle, forward and backward, on a bounded sample of token
+    rows of the same inputs (the backward's token reductions are linear in
+    the rows, so a row block does its share of every product)."""
     import numpy as np
 
     import oracle
@@ -131,6 +139,7 @@ def lora_cpu_baseline(cfg, d, budget_s):
     while time.perf_counter() - t0 < budget_s and done < M:
         x = f64_from_bf16_bits(d["x"][done:done + rows])
         oracle.lora_qkv_forward(x, Ws, ads, s)
+        oracle.lora_qkv_backward(x, Ws, ads, s, [f64_from_bf16_bits(g[done:done + rows]) for g in dy_bits])
         done += x.shape[0]
     dt = time.perf_counter() - t0
     try:
@@ -139,11 +148,11 @@ def lora_cpu_baseline(cfg, d, budget_s):
     except Exception:
         blas = []
     return {
-        "value": lora_flops(done, d_in, widths, r) / dt / 1e12,
+        "value": (lora_flops(done, d_in, widths, r) + lora_bwd_flops(done, d_in, widths, r)) / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": max([n for _, n in blas if n] or [1]),
         "kind": "oracle",
-        "sample": f"the first {done} of {M} token rows of {cfg['name']} (all three projections), float64 "
+        "sample": f"the first {done} of {M} token rows of {cfg['name']} (all three projections, forward + backward), float64 "
                   f"NumPy, {dt:.1f} s; rows do identical work, so the rate is the whole workload's",
         "host_cpus": len(os.sched_getaffinity(0)),
         "blas": blas,
@@ -170,32 +179,48 @@ def bench_lora(args, name):
     wt = [to_gpu(w) for w in d["wt"]]
     at = [to_gpu(a) for a in d["at"]]
     bt = [to_gpu(b) for b in d["bt"]]
+    dy_bits = workloads.make_lora_inputs(M, d_in, widths, r, seed=1, with_dy=True)["dy"]
+    dys = [to_gpu(g) for g in dy_bits]
     outs = tuple(torch.empty(M, w, dtype=torch.bfloat16, device=dev) for w in widths)
     ws = ops.lora_qkv_workspace(M, r, dev)
+    t = ws[: M * 3 * r * 2].view(torch.bfloat16).view(M, 3 * r)
+    grads = (torch.empty(M, d_in, dtype=torch.bfloat16, device=dev),
+             [torch.empty(r, d_in, dtype=torch.bfloat16, device=dev) for _ in range(3)],
+             [torch.empty(w, r, dtype=torch.bfloat16, device=dev) for w in widths])
+    wsb = ops.lora_qkv_bwd_workspace(M, d_in, widths[0], widths[1], r, dev)
     calib_copy(args, dev)
     stream = torch.cuda.current_stream(dev)
 
+    # One step: the projections forward, then their backward for a fixed
+    # upstream gradient (the training step of the prologue).
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
         ops.s2attn_lora_qkv_fwd(x, wt, at, bt, s, out=outs, workspace=ws)
         if ev is not None:
             ev[1].record(stream)
+        ops.s2attn_lora_qkv_bwd(x, wt, at, bt, s, t, dys, out=grads, workspace=wsb)
+        if ev is not None:
+            ev[2].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / max(args.steps, 1)
-    call_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    fl = lora_flops(M, d_in, widths, r)
-    value = fl / (ms_step * 1e-3) / 1e12
-    achieved = fl / (call_ms * 1e-3) / 1e12
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    ffl, bfl = lora_flops(M, d_in, widths, r), lora_bwd_flops(M, d_in, widths, r)
+    value = (ffl + bfl) / (ms_step * 1e-3) / 1e12
+    kernel_flops = {"lora_fwd_call": ffl, "lora_bwd_call": bfl}
+    kernel_ms = {"lora_fwd_call": fwd_ms, "lora_bwd_call": bwd_ms}
+    dominant = max(kernel_ms, key=kernel_ms.get)
+    achieved = kernel_flops[dominant] / (kernel_ms[dominant] * 1e-3) / 1e12
 
     # Context: the library GEMM (hipBLASLt through torch) for the frozen part
     # alone, all three weights concatenated into one [sum(widths), d_in].
@@ -229,17 +254,19 @@ def bench_lora(args, name):
         "config": {"workload": name, "M": M, "d_in": d_in, "widths": list(widths), "r": r, "scale": s,
                    "parallelism": "single-gpu"},
         "pct_peak": 100.0 * value / PEAK_BF16_TFLOPS,
-        "kernel_ms": {"lora_qkv_call": call_ms},
-        "roofline": {"bound": "mfma", "kernel": "lora_qkv_call", "achieved": achieved,
+        "fwd_tflops": ffl / (fwd_ms * 1e-3) / 1e12,
+        "bwd_tflops": bfl / (bwd_ms * 1e-3) / 1e12,
+        "kernel_ms": kernel_ms,
+        "roofline": {"bound": "mfma", "kernel": dominant, "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": None, "avg_launch_ms": call_ms},
-        "hbm_gbs_algorithmic": {"call": alg_bytes / (call_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS},
+                     "traffic": None, "avg_launch_ms": kernel_ms[dominant]},
+        "hbm_gbs_algorithmic": {"fwd_call": alg_bytes / (fwd_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS},
         "library_frozen_gemm": {"what": "torch F.linear (hipBLASLt) of x by the three frozen weights "
                                         "concatenated, no adapter", "ms": lib_ms, "tflops": lib_tf},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = lora_cpu_baseline(cfg, d, args.cpu_budget_s)
+        line["cpu_baseline"] = lora_cpu_baseline(cfg, d, dy_bits, args.cpu_budget_s)
     print(json.dumps(line), flush=True)
 
 

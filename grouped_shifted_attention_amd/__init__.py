@@ -24,4 +24,6 @@ from .ops import (  # noqa: F401
     s2attn_workspace_sizes,
     s2attn_lora_qkv_fwd,
     lora_qkv_workspace,
+    s2attn_lora_qkv_bwd,
+    lora_qkv_bwd_workspace,
 )

@@ -41,6 +41,9 @@ SIGNATURES = {
     "s2attn_lora_qkv_workspace_size": (_S, [_I, _I]),
     "s2attn_lora_qkv_fwd": (_I, [_P, _I, _I, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P, _P, _I, _D,
                                  _P, _P, _P, _P, _S, _P]),
+    "s2attn_lora_qkv_bwd_workspace_size": (_S, [_I, _I, _I, _I, _I]),
+    "s2attn_lora_qkv_bwd": (_I, [_P, _I, _I, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P, _P, _I, _D, _P,
+                                 _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P]),
     "s2attn_strerror": (ctypes.c_char_p, [_I]),
     "s2attn_last_error": (ctypes.c_char_p, []),
 }

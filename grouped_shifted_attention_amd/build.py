@@ -20,7 +20,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libs2attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["api.cpp", "fwd.hip", "bwd.hip", "bwd_delta.hip", "rope.hip", "lora_qkv.hip"]
+SOURCES = ["api.cpp", "fwd.hip", "bwd.hip", "bwd_delta.hip", "rope.hip", "lora_qkv.hip", "lora_bwd.hip"]
 HEADERS = ["device_common.hpp", "kernels.hpp", "staging.hpp", "lora_kernels.hpp"]
 
 ARCH = "gfx950"

@@ -3,6 +3,7 @@
 // GPU work and never lets an exception escape.
 #include "s2attn.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -426,6 +427,92 @@ int s2attn_lora_qkv_fwd(const void* x, int M, int d_in, const void* wq_t, const 
     a.t = r > 0 ? (uint16_t*)workspace : nullptr;
     hipError_t e = s2a::launch_lora_qkv(a, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "lora_qkv launch");
+    return (int)S2ATTN_OK;
+  });
+}
+
+size_t s2attn_lora_qkv_bwd_workspace_size(int M, int d_in, int width_q, int width_kv, int r) {
+  if (M <= 0 || r <= 0) return 0;
+  const size_t imax = (size_t)std::max(d_in, std::max(width_q, width_kv));
+  return round_up((size_t)M * 3 * r * 2) + round_up((size_t)s2a::lora_bwd_splits(M) * imax * r * 4);
+}
+
+int s2attn_lora_qkv_bwd(const void* x, int M, int d_in, const void* wq_t, const void* wk_t, const void* wv_t,
+                        int width_q, int width_kv, const void* aq_t, const void* ak_t, const void* av_t,
+                        const void* bq_t, const void* bk_t, const void* bv_t, int r, double scale, const void* t,
+                        const void* dq, const void* dk, const void* dv, void* dx, void* daq_t, void* dak_t,
+                        void* dav_t, void* dbq_t, void* dbk_t, void* dbv_t, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  return guarded([&] {
+    if (M < 0) return fail(S2ATTN_EINVAL, "M must be >= 0");
+    if (d_in < 64 || d_in % 64 != 0 || d_in > (1 << 20))
+      return fail(S2ATTN_EINVAL, "d_in must be a multiple of 64 in [64, 2^20]");
+    if (width_q < 64 || width_q % 64 != 0 || width_kv < 64 || width_kv % 64 != 0 || width_q > (1 << 20) ||
+        width_kv > (1 << 20))
+      return fail(S2ATTN_EINVAL, "width_q and width_kv must be multiples of 64 in [64, 2^20]");
+    if (r < 0 || r > 1024 || r % 8 != 0) return fail(S2ATTN_EINVAL, "r must be 0 or a multiple of 8 up to 1024");
+    if (!std::isfinite(scale)) return fail(S2ATTN_EINVAL, "scale must be finite");
+    if (std::ceil(M / 256.0) * std::ceil(std::max(d_in, std::max(width_q, width_kv)) / 256.0) > 2147483647.0 ||
+        (double)s2a::lora_bwd_splits(M) * std::ceil(std::max(d_in, std::max(width_q, width_kv)) / 128.0) * std::ceil(r / 64.0) >
+            2147483647.0)
+      return fail(S2ATTN_EINVAL, "too many work items for one launch");
+    if (M == 0) return (int)S2ATTN_OK;
+    const size_t xb = (size_t)M * d_in * 2;
+    const size_t wqb = (size_t)width_q * d_in * 2, wkb = (size_t)width_kv * d_in * 2;
+    const size_t ab = (size_t)r * d_in * 2, bqb = (size_t)width_q * r * 2, bkb = (size_t)width_kv * r * 2;
+    const size_t yqb = (size_t)M * width_q * 2, ykb = (size_t)M * width_kv * 2;
+    const size_t tb = (size_t)M * 3 * r * 2;
+    const size_t need = s2attn_lora_qkv_bwd_workspace_size(M, d_in, width_q, width_kv, r);
+    if (r > 0) {
+      if (workspace == nullptr) return fail(S2ATTN_EINVAL, "workspace is NULL");
+      if (workspace_bytes < need)
+        return fail(S2ATTN_EINVAL, "workspace too small: need " + std::to_string(need) + " bytes");
+      if (((uintptr_t)workspace & (kAlign - 1)) != 0) return fail(S2ATTN_EINVAL, "workspace is not 256-byte aligned");
+      const Buf in[] = {{x, xb, "x"},       {wq_t, wqb, "wq_t"}, {wk_t, wkb, "wk_t"}, {wv_t, wkb, "wv_t"},
+                        {aq_t, ab, "aq_t"}, {ak_t, ab, "ak_t"},  {av_t, ab, "av_t"},  {bq_t, bqb, "bq_t"},
+                        {bk_t, bkb, "bk_t"}, {bv_t, bkb, "bv_t"}, {t, tb, "t"},        {dq, yqb, "dq"},
+                        {dk, ykb, "dk"},    {dv, ykb, "dv"}};
+      const Buf out[] = {{dx, xb, "dx"},      {daq_t, ab, "daq_t"}, {dak_t, ab, "dak_t"},
+                         {dav_t, ab, "dav_t"}, {dbq_t, bqb, "dbq_t"}, {dbk_t, bkb, "dbk_t"},
+                         {dbv_t, bkb, "dbv_t"}, {workspace, need, "workspace"}};
+      int st = check_buffers(in, 14, out, 8);
+      if (st) return st;
+    } else {
+      const Buf in[] = {{x, xb, "x"},    {wq_t, wqb, "wq_t"}, {wk_t, wkb, "wk_t"}, {wv_t, wkb, "wv_t"},
+                        {dq, yqb, "dq"}, {dk, ykb, "dk"},     {dv, ykb, "dv"}};
+      const Buf out[] = {{dx, xb, "dx"}};
+      int st = check_buffers(in, 7, out, 1);
+      if (st) return st;
+    }
+    s2a::LoraQkvBwdArgs a{};
+    a.x = (const uint16_t*)x;
+    a.M = M;
+    a.K = d_in;
+    const void* wt[3] = {wq_t, wk_t, wv_t};
+    const void* at[3] = {aq_t, ak_t, av_t};
+    const void* bt[3] = {bq_t, bk_t, bv_t};
+    const void* dy[3] = {dq, dk, dv};
+    void* dat[3] = {daq_t, dak_t, dav_t};
+    void* dbt[3] = {dbq_t, dbk_t, dbv_t};
+    for (int p = 0; p < 3; ++p) {
+      a.wt[p] = (const uint16_t*)wt[p];
+      a.at[p] = r > 0 ? (const uint16_t*)at[p] : nullptr;
+      a.bt[p] = r > 0 ? (const uint16_t*)bt[p] : nullptr;
+      a.width[p] = p == 0 ? width_q : width_kv;
+      a.dy[p] = (const uint16_t*)dy[p];
+      a.dat[p] = r > 0 ? (uint16_t*)dat[p] : nullptr;
+      a.dbt[p] = r > 0 ? (uint16_t*)dbt[p] : nullptr;
+    }
+    a.r = r;
+    a.scale = (float)scale;
+    a.t = r > 0 ? (const uint16_t*)t : nullptr;
+    a.dx = (uint16_t*)dx;
+    if (r > 0) {
+      a.dts = (uint16_t*)workspace;
+      a.part = (float*)((char*)workspace + round_up(tb));
+    }
+    hipError_t e = s2a::launch_lora_qkv_bwd(a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "lora_qkv_bwd launch");
     return (int)S2ATTN_OK;
   });
 }

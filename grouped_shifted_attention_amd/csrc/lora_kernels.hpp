@@ -39,7 +39,61 @@ struct LoraGemmArgs {
   float scale;
 };
 
+// Backward.  A reduction segment of the token-by-weight product: token rows
+// tok[m][k] (row stride ldt) against weight rows w[k][n] (row stride ldw),
+// k < len; the weight rows come from w[0], w[1], w[2] in turn, `stack` rows
+// each (stack = len for a single weight).
+struct LoraBwdSeg {
+  const uint16_t* tok;
+  int ldt;
+  const uint16_t* w[3];
+  int ldw;
+  int len;
+  int stack;
+};
+
+// out[m][n] = scale * sum over segments of tok . w, m < M, n < N.
+struct LoraBwdK1Args {
+  int M, N;
+  uint16_t* out;
+  int ldo;
+  float scale;
+  int nseg;
+  LoraBwdSeg seg[4];
+};
+
+// part[split][j][i] = sum over the split's rows m of A[m][i] * B[m][j].
+struct LoraBwdK2Args {
+  const uint16_t* A;
+  int lda;
+  const uint16_t* B;
+  int ldb;
+  int M, I, J;
+  int rows_per_split;
+  float* part;
+};
+
+struct LoraQkvBwdArgs {
+  const uint16_t* x;      // [M, K]
+  int M, K;
+  const uint16_t* wt[3];  // W_p^T [width_p, K]
+  const uint16_t* at[3];  // A_p^T [r, K]
+  const uint16_t* bt[3];  // B_p^T [width_p, r]
+  int width[3];
+  int r;
+  float scale;
+  const uint16_t* t;      // the forward's s x A, [M, 3r]
+  const uint16_t* dy[3];  // upstream gradients [M, width_p]
+  uint16_t* dx;           // [M, K]
+  uint16_t* dat[3];       // dA_p^T [r, K]
+  uint16_t* dbt[3];       // dB_p^T [width_p, r]
+  uint16_t* dts;          // workspace [M, 3r]: s dy_p B_p^T
+  float* part;            // workspace: split partial sums
+};
+
 int lora_col_tiles(int width);
+int lora_bwd_splits(int M);
+hipError_t launch_lora_qkv_bwd(const LoraQkvBwdArgs& a, hipStream_t stream);
 hipError_t launch_lora_qkv(const LoraQkvArgs& a, hipStream_t stream);
 
 }  // namespace s2a

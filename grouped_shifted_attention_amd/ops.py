@@ -299,6 +299,58 @@ def s2attn_lora_qkv_fwd(x, wt, at=None, bt=None, scale=1.0, out=None, workspace=
     return out[0], out[1], out[2], ws
 
 
+def lora_qkv_bwd_workspace(M, d_in, width_q, width_kv, r, device):
+    """A workspace tensor large enough for s2attn_lora_qkv_bwd (None when r = 0)."""
+    n = lib().s2attn_lora_qkv_bwd_workspace_size(int(M), int(d_in), int(width_q), int(width_kv), int(r))
+    return None if n == 0 else _workspace(n, device)
+
+
+def s2attn_lora_qkv_bwd(x, wt, at, bt, scale, t, dys, out=None, workspace=None):
+    """Backward of s2attn_lora_qkv_fwd for upstream gradients dys = (dq, dk, dv).
+
+    x, wt, at, bt, scale as for the forward; t is the forward's low-rank
+    activations ([M, 3r] bf16, e.g. a view of the forward's workspace), or
+    None with r = 0.  Returns (dx [M, d_in], [dA_q^T, dA_k^T, dA_v^T] each
+    [r, d_in], [dB_q^T [width_q, r], dB_k^T, dB_v^T [width_kv, r]]); the
+    adapter lists are None when r = 0.
+    """
+    M, d_in = x.shape
+    dev = x.device
+    _need(x, "x", torch.bfloat16, (M, d_in), None)
+    wq, wkv = wt[0].shape[0], wt[1].shape[0]
+    widths = (wq, wkv, wkv)
+    for name, w, n in zip(("wq_t", "wk_t", "wv_t"), wt, widths):
+        _need(w, name, torch.bfloat16, (n, d_in), dev)
+    for name, d, n in zip(("dq", "dk", "dv"), dys, widths):
+        _need(d, name, torch.bfloat16, (M, n), dev)
+    if (at is None) != (bt is None):
+        raise ValueError("at and bt must both be given or both be None")
+    r = 0 if at is None else at[0].shape[0]
+    if r > 0:
+        for p in range(3):
+            _need(at[p], f"at[{p}]", torch.bfloat16, (r, d_in), dev)
+            _need(bt[p], f"bt[{p}]", torch.bfloat16, (widths[p], r), dev)
+        _need(t, "t", torch.bfloat16, (M, 3 * r), dev)
+    if out is None:
+        dx = torch.empty(M, d_in, dtype=torch.bfloat16, device=dev)
+        dat = [torch.empty(r, d_in, dtype=torch.bfloat16, device=dev) for _ in range(3)] if r > 0 else None
+        dbt = [torch.empty(n, r, dtype=torch.bfloat16, device=dev) for n in widths] if r > 0 else None
+    else:
+        dx, dat, dbt = out
+    _need(dx, "dx", torch.bfloat16, (M, d_in), dev)
+    ws = lora_qkv_bwd_workspace(M, d_in, wq, wkv, r, dev) if workspace is None else workspace
+    n3 = (None, None, None)
+    a3, b3 = (n3, n3) if r == 0 else (at, bt)
+    da3, db3 = (n3, n3) if r == 0 else (dat, dbt)
+    check(lib().s2attn_lora_qkv_bwd(
+        _ptr(x), M, d_in, _ptr(wt[0]), _ptr(wt[1]), _ptr(wt[2]), wq, wkv,
+        _ptr(a3[0]), _ptr(a3[1]), _ptr(a3[2]), _ptr(b3[0]), _ptr(b3[1]), _ptr(b3[2]), r, float(scale),
+        _ptr(t) if r > 0 else None, _ptr(dys[0]), _ptr(dys[1]), _ptr(dys[2]), _ptr(dx),
+        _ptr(da3[0]), _ptr(da3[1]), _ptr(da3[2]), _ptr(db3[0]), _ptr(db3[1]), _ptr(db3[2]),
+        _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(x)))
+    return dx, dat, dbt
+
+
 class S2AttnFunction(torch.autograd.Function):
     """Autograd wrapper: forward saves q, k, v, out and lse; backward calls the
     library's backward entry point."""

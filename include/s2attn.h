@@ -214,6 +214,35 @@ int s2attn_lora_qkv_fwd(const void* x, int M, int d_in,
                         void* q, void* k, void* v,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Backward of s2attn_lora_qkv_fwd (the calculus of its forward; the pages do
+ * not spell it out).  The pretrained W_p are frozen, so the call returns the
+ * input gradient and the adapters' gradients for upstream gradients dq, dk,
+ * dv ([M, width_q], [M, width_kv], [M, width_kv] bf16):
+ *   dx   = sum_p dy_p W_p^T + scale * (dy_p B_p^T) A_p^T     [M, d_in]
+ *   dA_p = scale * x^T (dy_p B_p^T)      written transposed, [r, d_in]
+ *   dB_p = (scale * x A_p)^T dy_p        written transposed, [width_p, r]
+ * `t` is the forward's low-rank activations (the first M * 3r bf16 of the
+ * forward's workspace after the call); dB is formed from it, so it carries
+ * the forward's bf16 rounding.  Weights, layouts and limits are those of
+ * s2attn_lora_qkv_fwd; outputs are overwritten.  With r = 0 only dx is
+ * computed and the adapter pointers, t and the workspace may be NULL.  The
+ * workspace (s2attn_lora_qkv_bwd_workspace_size() bytes, 256-byte aligned,
+ * clobbered) holds scale * dy_p B_p^T and the fixed-order partial sums of the
+ * token reductions; the result is deterministic.
+ */
+size_t s2attn_lora_qkv_bwd_workspace_size(int M, int d_in, int width_q, int width_kv, int r);
+int s2attn_lora_qkv_bwd(const void* x, int M, int d_in,
+                        const void* wq_t, const void* wk_t, const void* wv_t,
+                        int width_q, int width_kv,
+                        const void* aq_t, const void* ak_t, const void* av_t,
+                        const void* bq_t, const void* bk_t, const void* bv_t,
+                        int r, double scale, const void* t,
+                        const void* dq, const void* dk, const void* dv,
+                        void* dx, void* daq_t, void* dak_t, void* dav_t,
+                        void* dbq_t, void* dbk_t, void* dbv_t,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* s2attn_strerror(int status);
 

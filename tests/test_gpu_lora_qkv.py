@@ -144,3 +144,121 @@ def test_lora_qkv_full_size_sampled_rows(workload):
     for nm, y, ref, b in zip(("q", "k", "v"), ys, refs, bounds):
         _check(nm, to_f64(y.index_select(0, idx)), ref, b)
     _check("x A (workspace)", to_f64(t.index_select(0, idx)), t_ref, t_bound)
+
+
+# ------------------------------------------------------------------ backward
+#
+# Bar, derived like the forward's (u = 2^-8; an n-term fp32 sum is off by at
+# most n 2^-24 times the sum of its absolute terms, first order).  With
+# dTs = s dy B^T (exact), |dTs| its magnitude and S = s |dy| |B|^T the sum of
+# the absolute terms that form it (width terms), each element obeys
+#   dx  : u|dx| + u |dTs| |A| + width 2^-24 S |A| + n 2^-24 (|dy| |W| + |dTs| |A|),
+#         n = sum(width) + 3r
+#   dA^T: u|dA| + u |x|^T |dTs| + width 2^-24 |x|^T S + M 2^-24 |x|^T |dTs|
+#   dB^T: u|dB| + (u + M 2^-24) |T|^T |dy| + d_in 2^-24 (s |x| |A|)^T |dy|,  T = s x A
+# (the bf16 rounding of dTs and of the forward's T, the fp32 sums that form
+# them, the final sums and the output rounding).
+
+def _bwd_bounds(x, Ws, ads, dy, scale, rows=None):
+    """Oracle gradients and their bounds; dx only on `rows` when given."""
+    M, d_in = x.shape
+    xr = x if rows is None else x[rows]
+    n = sum(W.shape[1] for W in Ws) + 3 * ads[0][0].shape[1]
+    dx = np.zeros((xr.shape[0], d_in))
+    dxb = np.zeros_like(dx)
+    out = {}
+    for p, (W, (A, B), g) in enumerate(zip(Ws, ads, dy)):
+        width = W.shape[1]
+        gr = g if rows is None else g[rows]
+        dts = scale * (gr @ B.T)
+        S = abs(scale) * (np.abs(gr) @ np.abs(B).T)
+        dx += gr @ W.T + dts @ A.T
+        dxb += U * (np.abs(dts) @ np.abs(A).T) + width * 2.0 ** -24 * (S @ np.abs(A).T) \
+            + n * 2.0 ** -24 * (np.abs(gr) @ np.abs(W).T + np.abs(dts) @ np.abs(A).T)
+        if rows is None:
+            dA = x.T @ dts
+            ba = U * np.abs(dA) + (U + M * 2.0 ** -24) * (np.abs(x).T @ np.abs(dts)) \
+                + width * 2.0 ** -24 * (np.abs(x).T @ S)
+            T = scale * (x @ A)
+            dB = T.T @ g
+            bb = U * np.abs(dB) + (U + M * 2.0 ** -24) * (np.abs(T).T @ np.abs(g)) \
+                + d_in * 2.0 ** -24 * ((abs(scale) * (np.abs(x) @ np.abs(A))).T @ np.abs(g))
+            out[f"dA{p}"] = (dA.T, 1.01 * ba.T + 1e-30)
+            out[f"dB{p}"] = (dB.T, 1.01 * bb.T + 1e-30)
+    out["dx"] = (dx, 1.01 * (dxb + U * np.abs(dx)) + 1e-30)
+    return out
+
+
+def _bwd_call(d, r, scale):
+    x = to_gpu(d["x"])
+    wt = [to_gpu(w) for w in d["wt"]]
+    at = [to_gpu(a) for a in d["at"]] if r > 0 else None
+    bt = [to_gpu(b) for b in d["bt"]] if r > 0 else None
+    dys = [to_gpu(g) for g in d["dy"]]
+    _, _, _, ws = ops.s2attn_lora_qkv_fwd(x, wt, at, bt, scale)
+    t = ws[: x.shape[0] * 3 * r * 2].view(torch.bfloat16).view(x.shape[0], 3 * r) if r > 0 else None
+    dx, dat, dbt = ops.s2attn_lora_qkv_bwd(x, wt, at, bt, scale, t, dys)
+    torch.cuda.synchronize()
+    return dx, dat, dbt
+
+
+BWD_CASES = [c for c in CASES if c[0] != "single_token"] + [("single_token_bwd", 1, 128, 128, 64, 16, 1.0)]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=[c[0] for c in BWD_CASES])
+def test_lora_qkv_backward_small(case):
+    name, M, d_in, wq, wkv, r, scale = case
+    d = workloads.make_lora_inputs(M, d_in, (wq, wkv, wkv), r, seed=21, with_dy=True)
+    f = {"x": f64_from_bf16_bits(d["x"]), "wt": [f64_from_bf16_bits(w) for w in d["wt"]],
+         "at": [f64_from_bf16_bits(a) for a in d["at"]], "bt": [f64_from_bf16_bits(b) for b in d["bt"]]}
+    dy = [f64_from_bf16_bits(g) for g in d["dy"]]
+    dx, dat, dbt = _bwd_call(d, r, scale)
+    if r == 0:
+        assert dat is None and dbt is None
+    # The oracle's own backward is the reference; the bounds come from the
+    # same fp64 products.
+    Ws = [w.T for w in f["wt"]]
+    ads = [(a.T, b.T) for a, b in zip(f["at"], f["bt"])]  # r = 0: empty adapters
+    ref_dx, ref_grads = oracle.lora_qkv_backward(f["x"], Ws, ads, scale, dy)
+    ref = _bwd_bounds(f["x"], Ws, ads, dy, scale)
+    assert np.allclose(ref["dx"][0], ref_dx, rtol=1e-10, atol=1e-10)
+    _check("dx", to_f64(dx), ref_dx, ref["dx"][1])
+    for p in range(3 if r > 0 else 0):
+        _check(f"dA_{'qkv'[p]}^T", to_f64(dat[p]), ref_grads[p][0].T, ref[f"dA{p}"][1])
+        _check(f"dB_{'qkv'[p]}^T", to_f64(dbt[p]), ref_grads[p][1].T, ref[f"dB{p}"][1])
+
+
+def test_lora_qkv_backward_deterministic():
+    M, d_in, wq, wkv, r = 3000, 256, 256, 128, 16
+    d = workloads.make_lora_inputs(M, d_in, (wq, wkv, wkv), r, seed=22, with_dy=True)
+    a = _bwd_call(d, r, 1.0)
+    b = _bwd_call(d, r, 1.0)
+    assert torch.equal(a[0], b[0])
+    for p in range(3):
+        assert torch.equal(a[1][p], b[1][p]) and torch.equal(a[2][p], b[2][p])
+
+
+@pytest.mark.parametrize("workload", ["lora_qkv_llama2_7b_n32k"])
+def test_lora_qkv_backward_full_size(workload):
+    # dA and dB reduce over every token, so they are compared in full; dx on
+    # sampled token rows.
+    w = workloads.LORA_WORKLOADS[workload]
+    M, d_in, (wq, wkv, _), r, scale = w["M"], w["d_in"], w["widths"], w["r"], w["scale"]
+    d = workloads.make_lora_inputs(M, d_in, (wq, wkv, wkv), r, seed=0, with_dy=True)
+    dx, dat, dbt = _bwd_call(d, r, scale)
+    x = f64_from_bf16_bits(d["x"])
+    Ws = [f64_from_bf16_bits(w_).T for w_ in d["wt"]]
+    ads = [(f64_from_bf16_bits(a).T, f64_from_bf16_bits(b).T) for a, b in zip(d["at"], d["bt"])]
+    dy = [f64_from_bf16_bits(g) for g in d["dy"]]
+    rng = np.random.default_rng(6)
+    rows = np.unique(np.concatenate([[0, 255, 256, M // 2, M - 1], rng.integers(0, M, 27)]))
+    ref = _bwd_bounds(x, Ws, ads, dy, scale)          # dA, dB in full
+    refx = _bwd_bounds(x, Ws, ads, dy, scale, rows)   # dx on the sampled rows
+    # The oracle on the sampled rows agrees with the bound helper's products.
+    ox, _ = oracle.lora_qkv_backward(x[rows], Ws, ads, scale, [g[rows] for g in dy])
+    assert np.allclose(refx["dx"][0], ox, rtol=1e-10, atol=1e-10)
+    for p in range(3):
+        _check(f"dA_{'qkv'[p]}^T", to_f64(dat[p]), *ref[f"dA{p}"])
+        _check(f"dB_{'qkv'[p]}^T", to_f64(dbt[p]), *ref[f"dB{p}"])
+    idx = torch.from_numpy(rows).to("cuda:0")
+    _check("dx (sampled rows)", to_f64(dx.index_select(0, idx)), *refx["dx"])
