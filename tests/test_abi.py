@@ -222,3 +222,42 @@ def test_lora_without_adapter_needs_no_workspace():
     # r = 0 with NULL adapters and workspace passes validation; M = 0 keeps it
     # from launching.
     assert _lora(M=0, r=0, aq=None, ak=None, av=None, bq=None, bk=None, bv=None, ws=False) == _lib.S2ATTN_OK
+
+
+def _lora_bwd(M=512, d_in=128, wq=256, wkv=128, r=16, scale=1.0, ws=True, ws_bytes=None, **ptrs):
+    L = _lib.lib()
+    need = L.s2attn_lora_qkv_bwd_workspace_size(M, d_in, wq, wkv, r)
+    names = ("x", "wq", "wk", "wv", "aq", "ak", "av", "bq", "bk", "bv", "t", "dq", "dk", "dv",
+             "dx", "daq", "dak", "dav", "dbq", "dbk", "dbv", "ws")
+    p = {n: FAKE + i * (1 << 28) for i, n in enumerate(names)}
+    p.update(ptrs)
+    return L.s2attn_lora_qkv_bwd(p["x"], M, d_in, p["wq"], p["wk"], p["wv"], wq, wkv,
+                                 p["aq"], p["ak"], p["av"], p["bq"], p["bk"], p["bv"], r, scale, p["t"],
+                                 p["dq"], p["dk"], p["dv"], p["dx"], p["daq"], p["dak"], p["dav"],
+                                 p["dbq"], p["dbk"], p["dbv"], p["ws"] if ws else None,
+                                 need if ws_bytes is None else ws_bytes, None)
+
+
+def test_lora_bwd_workspace_size():
+    L = _lib.lib()
+    # s x A-sized bf16 block, then 1 split x max(d_in, widths) x r fp32 partials.
+    assert L.s2attn_lora_qkv_bwd_workspace_size(1000, 128, 256, 128, 16) == 96000 + 16384
+    assert L.s2attn_lora_qkv_bwd_workspace_size(1000, 128, 256, 128, 0) == 0
+    assert L.s2attn_lora_qkv_bwd_workspace_size(0, 128, 256, 128, 16) == 0
+
+
+@pytest.mark.parametrize("kw", [
+    dict(M=-1), dict(d_in=96), dict(wq=100), dict(wkv=0), dict(r=12), dict(r=2048), dict(scale=float("nan")),
+])
+def test_lora_bwd_rejects_bad_shapes(kw):
+    assert _lora_bwd(**kw) == EINVAL
+
+
+def test_lora_bwd_rejects_bad_buffers():
+    assert _lora_bwd(t=None) == EINVAL                        # r > 0 needs the forward's x A
+    assert _lora_bwd(dbv=None) == EINVAL
+    assert _lora_bwd(ws=False) == EINVAL
+    assert _lora_bwd(ws_bytes=1000) == EINVAL
+    assert _lora_bwd(dx=FAKE + 11 * (1 << 28)) == EINVAL      # dx overlaps dq
+    assert b"overlaps" in _lib.lib().s2attn_last_error()
+    assert _lora_bwd(M=0) == _lib.S2ATTN_OK
