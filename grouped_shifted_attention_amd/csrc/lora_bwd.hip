@@ -54,12 +54,25 @@ struct TrLane {
 // ---------------------------------------------------------------------------
 // K1: out[m][n] = scale * sum_segments sum_k tok[m][k] * w[k][n]
 // ---------------------------------------------------------------------------
-constexpr int kBM = 256, kBN = 256, kBK = 64;
+constexpr int kBM = 256, kBK = 64;
 constexpr int kTokStride = kBK + 8;     // token tile row stride (elements)
-constexpr int kWStride = kBN + 32;      // weight tile row stride: 576 B = 64 mod 256
 constexpr int kTokElems = kBM * kTokStride;
-constexpr int kWElems = kBK * kWStride;
 constexpr int kBand = 8;
+
+// Output tile width BN: 256 (wide outputs; each wave 128 columns x 64
+// tokens) or 64 (rank-wide outputs; each wave 64 columns x 32 tokens).
+// Weight tile row stride BN + 32 elements: 576 or 192 bytes, whose first
+// four rows fall at distinct 64-byte offsets mod 256.
+template <int BN>
+struct K1Shape {
+  static constexpr int WStride = BN + 32;
+  static constexpr int WElems = kBK * WStride;
+  static constexpr int NI = BN == 256 ? 4 : 2;  // 32-column tiles per wave
+  static constexpr int NJ = BN == 256 ? 2 : 1;  // 32-token tiles per wave
+  static constexpr int WO = BN / (32 * NI);     // waves along the columns
+  static constexpr int WChunks = BN / 8;        // 16-byte chunks per weight row
+  static constexpr int WPer = kBK * WChunks / 512;
+};
 
 __device__ __forceinline__ void tile_coords(int id, int mt, int nt, int& tm, int& tn) {
   const int band = id / (kBand * nt);
@@ -69,16 +82,20 @@ __device__ __forceinline__ void tile_coords(int id, int mt, int nt, int& tm, int
   tm = band * kBand + (rem - tn * rows);
 }
 
+template <int BN>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void lora_bwd_k1(LoraBwdK1Args a) {
+  using Sh = K1Shape<BN>;
+  constexpr int kBN = BN;
+  constexpr int kWStride = Sh::WStride;
   __shared__ __attribute__((aligned(16))) uint16_t X0[kTokElems];
   __shared__ __attribute__((aligned(16))) uint16_t X1[kTokElems];
-  __shared__ __attribute__((aligned(16))) uint16_t W0[kWElems];
-  __shared__ __attribute__((aligned(16))) uint16_t W1[kWElems];
+  __shared__ __attribute__((aligned(16))) uint16_t W0[Sh::WElems];
+  __shared__ __attribute__((aligned(16))) uint16_t W1[Sh::WElems];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int mt = (a.M + kBM - 1) / kBM;
-  const int nt = (a.N + kBN - 1) / kBN;
+  const int nt = (a.N + BN - 1) / BN;
   int tm, tn;
   tile_coords(xcd_logical_id(blockIdx.x, mt * nt), mt, nt, tm, tn);
   const int m0 = tm * kBM, n0 = tn * kBN;
@@ -90,11 +107,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int kt_total = ntiles[0] + ntiles[1] + ntiles[2] + ntiles[3];
 
   // Staging map.  Token tile: chunk tc = tid%8 of rows tid/8 + 64 i.  Weight
-  // tile: chunk wc = tid%32 (8 columns) of k rows tid/32 + 16 i.
+  // tile: chunk wc (8 columns) of k rows wrow + (512 / chunks per row) i.
   const int tc = tid & 7, trow = tid >> 3;
-  const int wc = tid & 31, wrow = tid >> 5;
+  const int wc = tid % Sh::WChunks, wrow = tid / Sh::WChunks;
+  constexpr int kWRowStep = 512 / Sh::WChunks;
   const int ncol = min(n0 + wc * 8, a.N - 8);  // clamped column (never stored past N)
-  u32x4 xr[4], wr[4];
+  u32x4 xr[4], wr[Sh::WPer];
   auto gload = [&](int kt) {
     // Segment of tile kt (wave-uniform; selected field by field so the
     // parameter block stays in scalar registers).
@@ -113,8 +131,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       xr[i] = ok ? v : zero_u4();
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int k = k0 + wrow + 16 * i;
+    for (int i = 0; i < Sh::WPer; ++i) {
+      const int k = k0 + wrow + kWRowStep * i;
       const bool ok = k < g.len;
       const int kk = ok ? k : 0;
       const int p = kk / g.stack;  // stacked weights: g.stack rows per pointer
@@ -125,34 +143,35 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
   auto swrite = [&](uint16_t* xs, uint16_t* ws) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<u32x4*>(xs + (trow + 64 * i) * kTokStride + tc * 8) = xr[i];
-      *reinterpret_cast<u32x4*>(ws + (wrow + 16 * i) * kWStride + wc * 8) = wr[i];
-    }
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(xs + (trow + 64 * i) * kTokStride + tc * 8) = xr[i];
+#pragma unroll
+    for (int i = 0; i < Sh::WPer; ++i)
+      *reinterpret_cast<u32x4*>(ws + (wrow + kWRowStep * i) * kWStride + wc * 8) = wr[i];
   };
 
-  // Wave tile: output columns wo*128 + 32 i (A operands, transposing reads),
-  // tokens wt*64 + 32 j (B operands, row reads).
-  const int wo = wave & 1, wt = wave >> 1;
+  // Wave tile: output columns wo*32*NI + 32 i (A operands, transposing
+  // reads), tokens wt*32*NJ + 32 j (B operands, row reads).
+  constexpr int NI = Sh::NI, NJ = Sh::NJ;
+  const int wo = wave % Sh::WO, wt = wave / Sh::WO;
   const TrLane tr(lane, kWStride);
-  const int b_off = (wt * 64 + (lane & 31)) * kTokStride + 8 * (lane >> 5);
-  f32x16 acc[4][2];
+  const int b_off = (wt * 32 * NJ + (lane & 31)) * kTokStride + 8 * (lane >> 5);
+  f32x16 acc[NI][NJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = zero16();
+    for (int j = 0; j < NJ; ++j) acc[i][j] = zero16();
   auto compute = [&](const uint16_t* xs, const uint16_t* ws) {
 #pragma unroll
     for (int kk = 0; kk < kBK / 16; ++kk) {
-      bf16x8 af[4], bfr[2];
+      bf16x8 af[NI], bfr[NJ];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = tr.read(ws, kWStride, kk * 16, wo * 128 + 32 * i);
+      for (int i = 0; i < NI; ++i) af[i] = tr.read(ws, kWStride, kk * 16, wo * 32 * NI + 32 * i);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) bfr[j] = lds_frag(xs + b_off + j * 32 * kTokStride + kk * 16);
+      for (int j = 0; j < NJ; ++j) bfr[j] = lds_frag(xs + b_off + j * 32 * kTokStride + kk * 16);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < NI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(af[i], bfr[j], acc[i][j]);
+        for (int j = 0; j < NJ; ++j) acc[i][j] = mfma32x32x16(af[i], bfr[j], acc[i][j]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -176,14 +195,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // Epilogue: lane = token, 4 runs of 4 consecutive output columns per tile.
   const float sc = a.scale;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int m = m0 + wt * 64 + 32 * j + (lane & 31);
+  for (int j = 0; j < NJ; ++j) {
+    const int m = m0 + wt * 32 * NJ + 32 * j + (lane & 31);
     if (m >= a.M) continue;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NI; ++i) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wo * 128 + 32 * i + 8 * g + 4 * (lane >> 5);
+        const int n = n0 + wo * 32 * NI + 32 * i + 8 * g + 4 * (lane >> 5);
         if (n < a.N) {
           const f32x16& v = acc[i][j];
           st8(a.out + (long long)m * a.ldo + n,
@@ -292,10 +311,11 @@ __global__ __launch_bounds__(256) void lora_bwd_k3(const float* __restrict__ par
   out[i * si + j * sj] = (uint16_t)(w[0] & 0xffffu);
 }
 
+template <int BN>
 hipError_t launch_k1(const LoraBwdK1Args& a, hipStream_t stream) {
-  const long long grid = (long long)((a.M + kBM - 1) / kBM) * ((a.N + kBN - 1) / kBN);
+  const long long grid = (long long)((a.M + kBM - 1) / kBM) * ((a.N + BN - 1) / BN);
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(lora_bwd_k1, dim3((unsigned)grid), dim3(512), 0, stream, a);
+  hipLaunchKernelGGL(lora_bwd_k1<BN>, dim3((unsigned)grid), dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -333,7 +353,7 @@ hipError_t launch_lora_qkv_bwd(const LoraQkvBwdArgs& q, hipStream_t stream) {
       k.scale = q.scale;
       k.nseg = 1;
       k.seg[0] = LoraBwdSeg{q.dy[p], q.width[p], {q.bt[p], q.bt[p], q.bt[p]}, q.r, q.width[p], q.width[p]};
-      if ((e = launch_k1(k, stream)) != hipSuccess) return e;
+      if ((e = launch_k1<64>(k, stream)) != hipSuccess) return e;
     }
   }
   // dx = sum_p dy_p W_p^T (+ dT_s A^T).
@@ -347,7 +367,7 @@ hipError_t launch_lora_qkv_bwd(const LoraQkvBwdArgs& q, hipStream_t stream) {
   for (int p = 0; p < 3; ++p)
     k.seg[k.nseg++] = LoraBwdSeg{q.dy[p], q.width[p], {q.wt[p], q.wt[p], q.wt[p]}, q.K, q.width[p], q.width[p]};
   if (q.r > 0) k.seg[k.nseg++] = LoraBwdSeg{q.dts, 3 * q.r, {q.at[0], q.at[1], q.at[2]}, q.K, 3 * q.r, q.r};
-  if ((e = launch_k1(k, stream)) != hipSuccess) return e;
+  if ((e = launch_k1<256>(k, stream)) != hipSuccess) return e;
   if (q.r == 0) return hipSuccess;
   const int splits = lora_bwd_splits(q.M);
   const int rps = ((q.M + splits - 1) / splits + kK2K - 1) / kK2K * kK2K;
