@@ -471,8 +471,7 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
   // P wave: S = Q K^T - lse (log2 units; lane column = key, elements = rows
   // 8*(r/4) + 4*hh + r%4 of the step), P = exp2(S), publish P,
   // dV^T += dO^T P.
-  auto p_step = [&](int step, int i0, auto mask_tag, auto c) __attribute__((always_inline)) {
-    constexpr bool MASK = decltype(mask_tag)::value;
+  auto p_step = [&](int step, int i0, bool mask, auto c) __attribute__((always_inline)) {
     const uint16_t* qt = qbuf(c);
     const uint16_t* ot = obuf(c);
     const float* st = stats(c);
@@ -482,7 +481,7 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       float pv = fast_exp2(sc[r]);
-      if constexpr (MASK) {
+      if (mask) {
         const int row = i0 + acc_row(r, hh);
         if (kj > row || row >= s.G) pv = 0.f;
       }
@@ -569,24 +568,23 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
   // Iteration n (stage c = n & 3): the P wave does step n, the dS wave step
   // n-1; step n+1 is resident, step n+2 loads into the stage that held step
   // n-2.  nsteps+1 iterations in all, identical for every wave.
-  auto iter = [&](int n, auto c) __attribute__((always_inline)) {
+  // The two roles run separate copies of the loop (the role is fixed per
+  // wave), and every step runs the same instructions: steps that lie wholly
+  // before this pair's keys are not skipped but fully masked (P = 0, so they
+  // add exact zeros).  Without branches around the products the accumulators
+  // keep their registers across steps instead of being copied at every join.
+  auto iter = [&](int n, auto c, auto role) __attribute__((always_inline)) {
     constexpr int C = decltype(c)::value;
+    constexpr bool DS = decltype(role)::value;
 #if S2A_DKDV_VSTAGE
     if (n + 3 < nsteps) gload_step(std::integral_constant<int, (C + 1) & 1>{});
 #else
     if (n + 2 < nsteps) load_step(n + 2, std::integral_constant<int, (C + 2) & 3>{});
 #endif
-    if (!ds_wave) {
-      if (n < nsteps) {
-        const int kind = step_kind(cur_j);
-        const int i0 = key_start + cur_j * kBMQ;
-        if (kind == 2)
-          p_step(n, i0, std::false_type{}, c);
-        else if (kind == 1)
-          p_step(n, i0, std::true_type{}, c);
-      }
+    if constexpr (!DS) {
+      if (n < nsteps) p_step(n, key_start + cur_j * kBMQ, step_kind(cur_j) != 2, c);
     } else {
-      if (n >= 1 && step_kind(prev_j) != 0) ds_step(n - 1, std::integral_constant<int, (C + 3) & 3>{});
+      if (n >= 1) ds_step(n - 1, std::integral_constant<int, (C + 3) & 3>{});
     }
     prev_j = cur_j;
     cur_j = cur_j + 1 == steps_per_head ? 0 : cur_j + 1;
@@ -597,12 +595,18 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
 #endif
     lds_barrier();
   };
-  for (int n = 0; n <= nsteps; n += 4) {
-    iter(n, S0{});
-    if (n + 1 <= nsteps) iter(n + 1, S1{});
-    if (n + 2 <= nsteps) iter(n + 2, S2{});
-    if (n + 3 <= nsteps) iter(n + 3, S3{});
-  }
+  auto run = [&](auto role) __attribute__((always_inline)) {
+    for (int n = 0; n <= nsteps; n += 4) {
+      iter(n, S0{}, role);
+      if (n + 1 <= nsteps) iter(n + 1, S1{}, role);
+      if (n + 2 <= nsteps) iter(n + 2, S2{}, role);
+      if (n + 3 <= nsteps) iter(n + 3, S3{}, role);
+    }
+  };
+  if (ds_wave)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
 
   if (kvalid) {
     if (ds_wave)
