@@ -479,13 +479,13 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
     chain_mfma(sc, qt);
     float p[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float pv = fast_exp2(sc[r]);
-      if (mask) {
+    for (int r = 0; r < 16; ++r) p[r] = fast_exp2(sc[r]);
+    if (mask) {  // one uniform branch around the selects, none per element
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
         const int row = i0 + acc_row(r, hh);
-        if (kj > row || row >= s.G) pv = 0.f;
+        p[r] = (kj > row || row >= s.G) ? 0.f : p[r];
       }
-      p[r] = pv;
     }
     bf16x8 pb[2];
     pb[0] = cvt8(f32x8{p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]});
