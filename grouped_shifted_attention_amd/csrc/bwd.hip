@@ -480,7 +480,7 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
     float p[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) p[r] = fast_exp2(sc[r]);
-    if (mask) {  // one uniform branch around the selects, none per element
+    if (__builtin_expect(mask, 0)) {  // one uniform branch around the selects, none per element
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = i0 + acc_row(r, hh);
