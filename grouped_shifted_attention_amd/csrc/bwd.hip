@@ -477,6 +477,13 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
     const float* st = stats(c);
     f32x16 sc = row_stats(st);
     chain_mfma(sc, qt);
+    // dO^T fragments of the dV product, read before the exp2 work that
+    // needs the chain's result, so their LDS latency hides behind it.
+    bf16x8 ofr[2][D / 32];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) ofr[hf][db] = sw.tr(ot, hf * 16, db);
     float p[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) p[r] = fast_exp2(sc[r]);
@@ -493,13 +500,9 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
     Pbuf[step & 1][pair][0][lane] = __builtin_bit_cast(u32x4, pb[0]);
     Pbuf[step & 1][pair][1][lane] = __builtin_bit_cast(u32x4, pb[1]);
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      bf16x8 ofr[D / 32];
+    for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) ofr[db] = sw.tr(ot, hf * 16, db);
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) acc[db] = mfma32x32x16(ofr[db], pb[hf], acc[db]);
-    }
+      for (int db = 0; db < D / 32; ++db) acc[db] = mfma32x32x16(ofr[hf][db], pb[hf], acc[db]);
   };
 
   // dS wave (one step behind): dP = dO V^T - Delta, dS = P dP with the P
@@ -510,6 +513,12 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
     const float* st = stats(c);
     f32x16 dp = row_stats(st + kBMQ);
     chain_mfma(dp, ot);
+    // Q^T fragments of the dK product, read ahead of the dS work.
+    bf16x8 qfr[2][D / 32];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) qfr[hf][db] = sw.tr(qt, hf * 16, db);
     const bf16x8 pb0 = __builtin_bit_cast(bf16x8, Pbuf[step & 1][pair][0][lane]);
     const bf16x8 pb1 = __builtin_bit_cast(bf16x8, Pbuf[step & 1][pair][1][lane]);
     float ds[16];
@@ -519,13 +528,9 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
     dsb[0] = cvt8(f32x8{ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]});
     dsb[1] = cvt8(f32x8{ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]});
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      bf16x8 qfr[D / 32];
+    for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) qfr[db] = sw.tr(qt, hf * 16, db);
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) acc[db] = mfma32x32x16(qfr[db], dsb[hf], acc[db]);
-    }
+      for (int db = 0; db < D / 32; ++db) acc[db] = mfma32x32x16(qfr[hf][db], dsb[hf], acc[db]);
   };
 
   // Per q head: steps whose rows all precede this pair's keys contribute
