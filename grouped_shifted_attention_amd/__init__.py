@@ -26,4 +26,6 @@ from .ops import (  # noqa: F401
     lora_qkv_workspace,
     s2attn_lora_qkv_bwd,
     lora_qkv_bwd_workspace,
+    LoraQKVFunction,
+    lora_qkv,
 )

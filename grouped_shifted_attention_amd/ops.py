@@ -377,6 +377,36 @@ class S2AttnFunction(torch.autograd.Function):
         return dq, dk, dv, None, None, None
 
 
+class LoraQKVFunction(torch.autograd.Function):
+    """Autograd wrapper of the LoRA q/k/v projections: forward keeps the
+    low-rank activations the library leaves in its workspace; backward calls
+    s2attn_lora_qkv_bwd (the frozen weights get no gradient)."""
+
+    @staticmethod
+    def forward(ctx, x, wq_t, wk_t, wv_t, aq_t, ak_t, av_t, bq_t, bk_t, bv_t, scale):
+        wt, at, bt = (wq_t, wk_t, wv_t), (aq_t, ak_t, av_t), (bq_t, bk_t, bv_t)
+        q, k, v, ws = s2attn_lora_qkv_fwd(x, wt, at, bt, scale)
+        M, r = x.shape[0], aq_t.shape[0]
+        t = ws[: M * 3 * r * 2].view(torch.bfloat16).view(M, 3 * r)
+        ctx.save_for_backward(x, wq_t, wk_t, wv_t, aq_t, ak_t, av_t, bq_t, bk_t, bv_t, t)
+        ctx.scale = scale
+        return q, k, v
+
+    @staticmethod
+    def backward(ctx, dq, dk, dv):
+        x, wq_t, wk_t, wv_t, aq_t, ak_t, av_t, bq_t, bk_t, bv_t, t = ctx.saved_tensors
+        dx, dat, dbt = s2attn_lora_qkv_bwd(x, (wq_t, wk_t, wv_t), (aq_t, ak_t, av_t), (bq_t, bk_t, bv_t),
+                                           ctx.scale, t, (dq.contiguous(), dk.contiguous(), dv.contiguous()))
+        return (dx, None, None, None, dat[0], dat[1], dat[2], dbt[0], dbt[1], dbt[2], None)
+
+
+def lora_qkv(x, wt, at, bt, scale=1.0):
+    """LoRA-adapted q/k/v projections with autograd: returns (q, k, v) as
+    [M, width] tensors; gradients flow to x and to the adapters (A^T, B^T),
+    not to the frozen W^T."""
+    return LoraQKVFunction.apply(x, *wt, *at, *bt, float(scale))
+
+
 def s2attn(q, k, v, group_size, shift=None, rope=None):
     """S2-Attn with autograd.  shift defaults to group_size // 2 (the pages'
     half-group shift); rope is None or (rope_base, pos_scale)."""
