@@ -254,49 +254,53 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 // step behind on the same keys and computes dP = dO V^T, dS = P (dP - Delta)
 // and dK^T += Q^T dS.  Each keeps one of K/V and one of dK/dV, which halves
 // the registers a wave needs against one wave doing all four products.
-// q/dout tiles sit in a 4-deep LDS ring: while the two roles work on steps
-// n and n-1, step n+1 is resident and step n+2 is being loaded.  The rows'
-// lse and Delta ride along at the end of the dout tile.  One barrier per
-// step.
+// q/dout tiles sit in a 6-deep LDS ring and the dS wave runs two steps
+// behind the P wave, so the waves meet at a barrier only every second step:
+// in the two steps between barriers the P waves read steps n, n+1, the dS
+// waves steps n-2, n-1, and steps n+2, n+3 are written.  The rows' lse and
+// Delta ride along at the end of the dout tile; P travels through four LDS
+// slots (step & 3).
 constexpr int kDkdvPairs = 4;
 constexpr int kDkdvWaves = 2 * kDkdvPairs;
 constexpr int kBNK = kDkdvPairs * 32;  // keys per workgroup
 constexpr int kBMQ = 32;               // q rows per step
-constexpr int kStages = 4;
-#ifndef S2A_DKDV_VSTAGE
-#define S2A_DKDV_VSTAGE 1  // q/dout tiles staged through VGPRs (1) or loaded straight into LDS (0)
-#endif
+constexpr int kStages = 6;
 
 template <int D, bool ROPE>
 __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void dkdv_kernel(
     BwdArgs a, RopeTable rope) {
   using TileStage = LdsStage<D, kBMQ, kDkdvWaves>;
-  // The ring's q and dout tiles are eight distinct LDS objects, each named
-  // at compile time (step m in stage m & 3), so reads of one stage never
-  // wait for the direct loads into another.
+  // The ring's q and dout tiles are twelve distinct LDS objects, each named
+  // at compile time (step m in stage m % 6).
   __shared__ __attribute__((aligned(16))) uint16_t Q0[TileStage::ELEMS];
   __shared__ __attribute__((aligned(16))) uint16_t Q1[TileStage::ELEMS];
   __shared__ __attribute__((aligned(16))) uint16_t Q2[TileStage::ELEMS];
   __shared__ __attribute__((aligned(16))) uint16_t Q3[TileStage::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t Q4[TileStage::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t Q5[TileStage::ELEMS];
   // dout tile, then the step's 32 lse values and 32 Delta values (fp32).
   constexpr int kOElems = TileStage::ELEMS + 2 * kBMQ * 2;
   __shared__ __attribute__((aligned(16))) uint16_t O0[kOElems];
   __shared__ __attribute__((aligned(16))) uint16_t O1[kOElems];
   __shared__ __attribute__((aligned(16))) uint16_t O2[kOElems];
   __shared__ __attribute__((aligned(16))) uint16_t O3[kOElems];
+  __shared__ __attribute__((aligned(16))) uint16_t O4[kOElems];
+  __shared__ __attribute__((aligned(16))) uint16_t O5[kOElems];
   auto qbuf = [&](auto c) __attribute__((always_inline)) -> uint16_t* {
     constexpr int C = decltype(c)::value;
     if constexpr (C == 0) return Q0; else if constexpr (C == 1) return Q1;
-    else if constexpr (C == 2) return Q2; else return Q3;
+    else if constexpr (C == 2) return Q2; else if constexpr (C == 3) return Q3;
+    else if constexpr (C == 4) return Q4; else return Q5;
   };
   auto obuf = [&](auto c) __attribute__((always_inline)) -> uint16_t* {
     constexpr int C = decltype(c)::value;
     if constexpr (C == 0) return O0; else if constexpr (C == 1) return O1;
-    else if constexpr (C == 2) return O2; else return O3;
+    else if constexpr (C == 2) return O2; else if constexpr (C == 3) return O3;
+    else if constexpr (C == 4) return O4; else return O5;
   };
-  static_assert(kStages == 4, "the ring is unrolled by four");
-  // P hand-over: [buffer][pair][half][lane] 16 bytes (8 bf16).
-  __shared__ __attribute__((aligned(16))) u32x4 Pbuf[2][kDkdvPairs][2][64];
+  static_assert(kStages == 6, "the ring is unrolled by six");
+  // P hand-over: [slot][pair][half][lane] 16 bytes (8 bf16); step m in slot m & 3.
+  __shared__ __attribute__((aligned(16))) u32x4 Pbuf[4][kDkdvPairs][2][64];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep it scalar
@@ -348,44 +352,13 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
   auto stats = [&](auto c) __attribute__((always_inline)) -> float* {
     return reinterpret_cast<float*>(obuf(c) + TileStage::ELEMS);
   };
-  // q and dout rows of a step go straight into LDS, and wave 0 loads the
-  // rows' lse (lanes 0-31) and Delta (lanes 32-63) behind the dout tile.
-  // Rows past the group end point at the group's last row; the P wave
-  // masks them.
-  auto load_step = [&](int step, auto c) __attribute__((always_inline)) {
-    const int hi = step / steps_per_head;
-    const int i0 = key_start + (step - hi * steps_per_head) * kBMQ;
-    const int h = h0 + hi;
-    const long long head_off = (long long)b * s.N * q_row + (long long)h * D;
-    const uint16_t* qt = contig_tile(a.q + head_off, q_row, base, i0, kBMQ, s.G, s.N);
-    if (qt != nullptr) {
-      ts.load_contig(qt, qbuf(c), wave);
-      ts.load_contig(a.dout + (qt - a.q), obuf(c), wave);
-    } else {
-      auto rows = [&](const uint16_t* head0) {
-        return [=, &s](int row) {
-          const int i = min(i0 + row, s.G - 1);
-          return head0 + orig_pos(base, i, s.N) * q_row;
-        };
-      };
-      ts.load_rows(rows(a.q + head_off), qbuf(c), wave, lane);
-      ts.load_rows(rows(a.dout + head_off), obuf(c), wave, lane);
-    }
-    if (wave == 0) {
-      const int i = min(i0 + rowperm32(l32), s.G - 1);  // slot m holds tile row rowperm32(m)
-      const long long so = ((long long)b * s.H + h) * s.N + orig_pos(base, i, s.N);
-      dma4((hh ? a.ndelta : a.nlse2) + so, stats(c));
-    }
-  };
-
-#if S2A_DKDV_VSTAGE
-  // Staging through VGPRs instead: thread tid owns 16-byte chunks tid,
+  // Staging through VGPRs: thread tid owns 16-byte chunks tid,
   // tid + 512, ... of the step's q tile followed by its dout tile (chunk =
   // tile row * D/8 + column chunk); wave 0 also loads the rows' statistics
   // (lanes 0-31 -lse*log2 e, lanes 32-63 -Delta, slot m holding tile row
   // rowperm32(m)).  Two register sets (step m in set m & 1): the loads of
-  // step n+3 are issued at the start of iteration n and written to LDS at
-  // the end of iteration n+1, so they have two iterations to arrive.
+  // step n+3 are issued at the start of step n and written to LDS at the
+  // end of step n+1, so they have two steps to arrive.
   constexpr int kCh = D / 8;
   constexpr int kChunks = kBMQ * kCh;  // per tensor
   constexpr int kThreads = kDkdvWaves * 64;
@@ -431,7 +404,6 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
     }
     if (wave == 0) stats(c)[lane] = stg_stat[R];
   };
-#endif
 
   // Accumulator start values for a step: element r of the lane belongs to
   // row slot 8*(r/4) + 4*hh + r%4, whose statistic sits at that slot.
@@ -497,15 +469,15 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
     bf16x8 pb[2];
     pb[0] = cvt8(f32x8{p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]});
     pb[1] = cvt8(f32x8{p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]});
-    Pbuf[step & 1][pair][0][lane] = __builtin_bit_cast(u32x4, pb[0]);
-    Pbuf[step & 1][pair][1][lane] = __builtin_bit_cast(u32x4, pb[1]);
+    Pbuf[step & 3][pair][0][lane] = __builtin_bit_cast(u32x4, pb[0]);
+    Pbuf[step & 3][pair][1][lane] = __builtin_bit_cast(u32x4, pb[1]);
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) acc[db] = mfma32x32x16(ofr[hf][db], pb[hf], acc[db]);
   };
 
-  // dS wave (one step behind): dP = dO V^T - Delta, dS = P dP with the P
+  // dS wave (two steps behind): dP = dO V^T - Delta, dS = P dP with the P
   // wave's published P, dK^T += Q^T dS.
   auto ds_step = [&](int step, auto c) __attribute__((always_inline)) {
     const uint16_t* qt = qbuf(c);
@@ -519,8 +491,8 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) qfr[hf][db] = sw.tr(qt, hf * 16, db);
-    const bf16x8 pb0 = __builtin_bit_cast(bf16x8, Pbuf[step & 1][pair][0][lane]);
-    const bf16x8 pb1 = __builtin_bit_cast(bf16x8, Pbuf[step & 1][pair][1][lane]);
+    const bf16x8 pb0 = __builtin_bit_cast(bf16x8, Pbuf[step & 3][pair][0][lane]);
+    const bf16x8 pb1 = __builtin_bit_cast(bf16x8, Pbuf[step & 3][pair][1][lane]);
     float ds[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) ds[r] = (float)(r < 8 ? pb0[r] : pb1[r - 8]) * dp[r];
@@ -543,17 +515,12 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
   auto step_kind = [&](int j) __attribute__((always_inline)) {  // 0 skip, 1 masked, 2 full
     return j < skip ? 0 : ((j < diag_end || j >= ragged) ? 1 : 2);
   };
-  int cur_j = 0, prev_j = 0;  // j of step n (P wave) and of step n-1 (dS wave)
+  int cur_j = 0;  // j of step n (P wave)
 
-  const int loads_per_step = 2 * TileStage::count(wave) + (wave == 0 ? 1 : 0);
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
-  using S2 = std::integral_constant<int, 2>;
-  using S3 = std::integral_constant<int, 3>;
-#if S2A_DKDV_VSTAGE
-  (void)loads_per_step;
   using R0 = std::integral_constant<int, 0>;
   using R1 = std::integral_constant<int, 1>;
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
   if (nsteps > 0) {
     gload_step(R0{});
     swrite_step(S0{}, R0{});
@@ -563,16 +530,15 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
     swrite_step(S1{}, R1{});
   }
   if (nsteps > 2) gload_step(R0{});
-#else
-  if (nsteps > 0) load_step(0, S0{});
-  if (nsteps > 1) load_step(1, S1{});
-  wait_vmcnt_dyn(nsteps > 1 ? loads_per_step : 0);
-#endif
   lds_barrier();
 
-  // Iteration n (stage c = n & 3): the P wave does step n, the dS wave step
-  // n-1; step n+1 is resident, step n+2 loads into the stage that held step
-  // n-2.  nsteps+1 iterations in all, identical for every wave.
+  // Step n (stage c = n % 6): the P wave does step n, the dS wave step n-2;
+  // the loads of step n+3 are issued and step n+2 is written into the stage
+  // that held step n-4.  A barrier follows every odd step, so between two
+  // barriers (steps n, n+1 with n even) the reads touch steps n-2 .. n+1
+  // and the writes steps n+2, n+3 (P slots n & 3, n+1 & 3; read two steps
+  // later, across a barrier): six distinct stages, four distinct P slots.
+  // nsteps+2 steps in all, identical for every wave.
   // The two roles run separate copies of the loop (the role is fixed per
   // wave), and every step runs the same instructions: steps that lie wholly
   // before this pair's keys are not skipped but fully masked (P = 0, so they
@@ -581,31 +547,24 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
   auto iter = [&](int n, auto c, auto role) __attribute__((always_inline)) {
     constexpr int C = decltype(c)::value;
     constexpr bool DS = decltype(role)::value;
-#if S2A_DKDV_VSTAGE
     if (n + 3 < nsteps) gload_step(std::integral_constant<int, (C + 1) & 1>{});
-#else
-    if (n + 2 < nsteps) load_step(n + 2, std::integral_constant<int, (C + 2) & 3>{});
-#endif
     if constexpr (!DS) {
       if (n < nsteps) p_step(n, key_start + cur_j * kBMQ, step_kind(cur_j) != 2, c);
+      cur_j = cur_j + 1 == steps_per_head ? 0 : cur_j + 1;
     } else {
-      if (n >= 1) ds_step(n - 1, std::integral_constant<int, (C + 3) & 3>{});
+      if (n >= 2) ds_step(n - 2, std::integral_constant<int, (C + 4) % 6>{});
     }
-    prev_j = cur_j;
-    cur_j = cur_j + 1 == steps_per_head ? 0 : cur_j + 1;
-#if S2A_DKDV_VSTAGE
-    if (n + 2 < nsteps) swrite_step(std::integral_constant<int, (C + 2) & 3>{}, std::integral_constant<int, C & 1>{});
-#else
-    wait_vmcnt_dyn(n + 2 < nsteps ? loads_per_step : 0);
-#endif
-    lds_barrier();
+    if (n + 2 < nsteps) swrite_step(std::integral_constant<int, (C + 2) % 6>{}, std::integral_constant<int, C & 1>{});
+    if constexpr ((C & 1) != 0) lds_barrier();
   };
   auto run = [&](auto role) __attribute__((always_inline)) {
-    for (int n = 0; n <= nsteps; n += 4) {
-      iter(n, S0{}, role);
-      if (n + 1 <= nsteps) iter(n + 1, S1{}, role);
-      if (n + 2 <= nsteps) iter(n + 2, S2{}, role);
-      if (n + 3 <= nsteps) iter(n + 3, S3{}, role);
+    for (int n = 0; n <= nsteps + 1; n += 6) {
+      iter(n, std::integral_constant<int, 0>{}, role);
+      if (n + 1 <= nsteps + 1) iter(n + 1, std::integral_constant<int, 1>{}, role);
+      if (n + 2 <= nsteps + 1) iter(n + 2, std::integral_constant<int, 2>{}, role);
+      if (n + 3 <= nsteps + 1) iter(n + 3, std::integral_constant<int, 3>{}, role);
+      if (n + 4 <= nsteps + 1) iter(n + 4, std::integral_constant<int, 4>{}, role);
+      if (n + 5 <= nsteps + 1) iter(n + 5, std::integral_constant<int, 5>{}, role);
     }
   };
   if (ds_wave)
