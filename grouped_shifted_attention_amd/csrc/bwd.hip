@@ -471,10 +471,15 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
     pb[1] = cvt8(f32x8{p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]});
     Pbuf[step & 3][pair][0][lane] = __builtin_bit_cast(u32x4, pb[0]);
     Pbuf[step & 3][pair][1][lane] = __builtin_bit_cast(u32x4, pb[1]);
+    // Raised issue priority over the closing products: when both waves of a
+    // SIMD are ready, these MFMAs go first and the partner's VALU work fills
+    // the gaps between them.
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) acc[db] = mfma32x32x16(ofr[hf][db], pb[hf], acc[db]);
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // dS wave (two steps behind): dP = dO V^T - Delta, dS = P dP with the P
@@ -499,10 +504,12 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
     bf16x8 dsb[2];
     dsb[0] = cvt8(f32x8{ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]});
     dsb[1] = cvt8(f32x8{ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]});
+    __builtin_amdgcn_s_setprio(1);  // as in the P wave
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) acc[db] = mfma32x32x16(qfr[hf][db], dsb[hf], acc[db]);
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // Per q head: steps whose rows all precede this pair's keys contribute
