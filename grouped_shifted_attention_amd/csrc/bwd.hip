@@ -419,11 +419,11 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
   };
 
   // acc += T K^T (or T V^T) for the step's 32-row tile T in LDS: one
-  // dependent chain of D/16 MFMAs whose A fragments are read five k-steps
+  // dependent chain of D/16 MFMAs whose A fragments are read three k-steps
   // ahead (the compiler would otherwise put each read right before its MFMA
   // and expose the LDS latency at every k-step).
   auto chain_mfma = [&](f32x16& acc_, const uint16_t* t) __attribute__((always_inline)) {
-    constexpr int kPF = 6;  // fragments in flight
+    constexpr int kPF = 4;  // fragments in flight (4 timed best of 2, 3, 4, 6, 8)
     bf16x8 fa[kPF];
 #pragma unroll
     for (int kk = 0; kk < kPF - 1; ++kk) fa[kk] = sw.row(t, 0, kk);
