@@ -259,7 +259,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 // in the two steps between barriers the P waves read steps n, n+1, the dS
 // waves steps n-2, n-1, and steps n+2, n+3 are written.  The rows' lse and
 // Delta ride along at the end of the dout tile; P travels through four LDS
-// slots (step & 3).
+// slots (step & 3) as fp16, whose 11-bit significand keeps dS = P (dP -
+// Delta) from inheriting the 8-bit rounding of the bf16 P that feeds dV (P
+// lies in [0, 1], where fp16 is exact to 2^-11 relative down to 2^-14 and
+// to 2^-25 absolute below).
+//
+// The largest P and dS of a key sit in the rows just past it: the masked
+// (diagonal) step.  There the dV and dK products take their bf16 operand as
+// hi + lo (two MFMAs each), so their rounding error, which would otherwise
+// dominate the k/v gradients summed over grouped-query heads, drops to that
+// of an fp32 operand.  Masked steps are about one in G/128 per head.
 constexpr int kDkdvPairs = 4;
 constexpr int kDkdvWaves = 2 * kDkdvPairs;
 constexpr int kBNK = kDkdvPairs * 32;  // keys per workgroup
@@ -299,7 +308,7 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
     else if constexpr (C == 4) return O4; else return O5;
   };
   static_assert(kStages == 6, "the ring is unrolled by six");
-  // P hand-over: [slot][pair][half][lane] 16 bytes (8 bf16); step m in slot m & 3.
+  // P hand-over: [slot][pair][half][lane] 16 bytes (8 fp16); step m in slot m & 3.
   __shared__ __attribute__((aligned(16))) u32x4 Pbuf[4][kDkdvPairs][2][64];
 
   const int tid = threadIdx.x;
@@ -466,11 +475,13 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
         p[r] = (kj > row || row >= s.G) ? 0.f : p[r];
       }
     }
+    const f32x8 pf[2] = {f32x8{p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]},
+                         f32x8{p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]}};
     bf16x8 pb[2];
-    pb[0] = cvt8(f32x8{p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]});
-    pb[1] = cvt8(f32x8{p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]});
-    Pbuf[step & 3][pair][0][lane] = __builtin_bit_cast(u32x4, pb[0]);
-    Pbuf[step & 3][pair][1][lane] = __builtin_bit_cast(u32x4, pb[1]);
+    pb[0] = cvt8(pf[0]);
+    pb[1] = cvt8(pf[1]);
+    Pbuf[step & 3][pair][0][lane] = __builtin_bit_cast(u32x4, __builtin_convertvector(pf[0], f16x8));
+    Pbuf[step & 3][pair][1][lane] = __builtin_bit_cast(u32x4, __builtin_convertvector(pf[1], f16x8));
     // Raised issue priority over the closing products: when both waves of a
     // SIMD are ready, these MFMAs go first and the partner's VALU work fills
     // the gaps between them.
@@ -479,12 +490,20 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) acc[db] = mfma32x32x16(ofr[hf][db], pb[hf], acc[db]);
+    if (__builtin_expect(mask, 0)) {  // diagonal step: the part of P that bf16 missed
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const bf16x8 pl = bf16_residual8(pf[hf], pb[hf]);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) acc[db] = mfma32x32x16(ofr[hf][db], pl, acc[db]);
+      }
+    }
     __builtin_amdgcn_s_setprio(0);
   };
 
   // dS wave (two steps behind): dP = dO V^T - Delta, dS = P dP with the P
   // wave's published P, dK^T += Q^T dS.
-  auto ds_step = [&](int step, auto c) __attribute__((always_inline)) {
+  auto ds_step = [&](int step, bool mask, auto c) __attribute__((always_inline)) {
     const uint16_t* qt = qbuf(c);
     const uint16_t* ot = obuf(c);
     const float* st = stats(c);
@@ -496,19 +515,29 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) qfr[hf][db] = sw.tr(qt, hf * 16, db);
-    const bf16x8 pb0 = __builtin_bit_cast(bf16x8, Pbuf[step & 3][pair][0][lane]);
-    const bf16x8 pb1 = __builtin_bit_cast(bf16x8, Pbuf[step & 3][pair][1][lane]);
+    const f16x8 ph0 = __builtin_bit_cast(f16x8, Pbuf[step & 3][pair][0][lane]);
+    const f16x8 ph1 = __builtin_bit_cast(f16x8, Pbuf[step & 3][pair][1][lane]);
     float ds[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) ds[r] = (float)(r < 8 ? pb0[r] : pb1[r - 8]) * dp[r];
+    for (int r = 0; r < 16; ++r) ds[r] = (float)(r < 8 ? ph0[r] : ph1[r - 8]) * dp[r];
+    const f32x8 dsf[2] = {f32x8{ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]},
+                          f32x8{ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]}};
     bf16x8 dsb[2];
-    dsb[0] = cvt8(f32x8{ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]});
-    dsb[1] = cvt8(f32x8{ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]});
+    dsb[0] = cvt8(dsf[0]);
+    dsb[1] = cvt8(dsf[1]);
     __builtin_amdgcn_s_setprio(1);  // as in the P wave
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) acc[db] = mfma32x32x16(qfr[hf][db], dsb[hf], acc[db]);
+    if (__builtin_expect(mask, 0)) {  // diagonal step: the part of dS that bf16 missed
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const bf16x8 dl = bf16_residual8(dsf[hf], dsb[hf]);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) acc[db] = mfma32x32x16(qfr[hf][db], dl, acc[db]);
+      }
+    }
     __builtin_amdgcn_s_setprio(0);
   };
 
@@ -523,6 +552,7 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
     return j < skip ? 0 : ((j < diag_end || j >= ragged) ? 1 : 2);
   };
   int cur_j = 0;  // j of step n (P wave)
+  int ds_j = 0;   // j of step n - 2 (dS wave)
 
   using R0 = std::integral_constant<int, 0>;
   using R1 = std::integral_constant<int, 1>;
@@ -559,7 +589,10 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
       if (n < nsteps) p_step(n, key_start + cur_j * kBMQ, step_kind(cur_j) != 2, c);
       cur_j = cur_j + 1 == steps_per_head ? 0 : cur_j + 1;
     } else {
-      if (n >= 2) ds_step(n - 2, std::integral_constant<int, (C + 4) % 6>{});
+      if (n >= 2) {
+        ds_step(n - 2, step_kind(ds_j) != 2, std::integral_constant<int, (C + 4) % 6>{});
+        ds_j = ds_j + 1 == steps_per_head ? 0 : ds_j + 1;
+      }
     }
     if (n + 2 < nsteps) swrite_step(std::integral_constant<int, (C + 2) % 6>{}, std::integral_constant<int, C & 1>{});
     if constexpr ((C & 1) != 0) lds_barrier();

@@ -25,6 +25,7 @@ typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -52,6 +53,12 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 
 // Round 8 floats to bf16 (round-to-nearest-even, v_cvt_pk_bf16_f32).
 __device__ __forceinline__ bf16x8 cvt8(f32x8 x) { return __builtin_convertvector(x, bf16x8); }
+// The part of x that its bf16 rounding hi misses, itself rounded to bf16:
+// hi + lo carries x to about 16 significant bits, so a product taken as
+// A*hi + A*lo on bf16 MFMA is as accurate as one with an fp32 operand.
+__device__ __forceinline__ bf16x8 bf16_residual8(f32x8 x, bf16x8 hi) {
+  return cvt8(x - __builtin_convertvector(hi, f32x8));
+}
 __device__ __forceinline__ u32x2 cvt4_bits(float a, float b, float c, float d) {
   f32x4 x = {a, b, c, d};
   return __builtin_bit_cast(u32x2, __builtin_convertvector(x, bf16x4));

@@ -1,9 +1,13 @@
 """GPU parity at the full workload sizes, in the launch configuration the
 benchmark times.
 
-The oracle computes sampled units (batch, head, group) one by one: both head
-halves, the first group and the wrap group of the shifted heads.  Groups are
-independent, so a sampled unit's rows are compared exactly with the oracle's.
+The oracle computes sampled units (batch, head, group) one by one: the first
+and last head of each half (H/2 - 1 and H/2 are the last unshifted and the
+first shifted head) in the first group and in the last group, which for the
+shifted heads is the wrap group.  Under grouped-query sharing the k/v
+gradients are compared per (k/v head, group) with all the q heads that read
+that k/v head.  Groups are independent, so a sampled unit's rows are
+compared exactly with the oracle's.
 The whole gradient tensors are additionally checked against invariants that
 need no oracle: per (k/v head, group), the key gradients of the rotated keys
 sum to zero (softmax rows of dS sum to zero) and the value gradients sum to
@@ -17,7 +21,7 @@ import torch
 import oracle
 import workloads
 from grouped_shifted_attention_amd import ops
-from gpu_helpers import LSE_MAX_ABS, assert_close, kv_grad_max_abs, to_f64, to_gpu
+from gpu_helpers import LSE_MAX_ABS, assert_close, to_f64, to_gpu
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
 
@@ -83,9 +87,8 @@ class Run:
                 idx = torch.from_numpy(pos).cuda()
                 assert_close(f"dq[h{h},g{g}]", to_f64(self.dq[0, :, h][idx]), uq)
         idx = torch.from_numpy(pos).cuda()
-        bar = kv_grad_max_abs(self.H, self.Hkv)
-        assert_close(f"dk[kv{kvh},g{g}]", to_f64(self.dk[0, :, kvh][idx]), dk, max_abs=bar)
-        assert_close(f"dv[kv{kvh},g{g}]", to_f64(self.dv[0, :, kvh][idx]), dv, max_abs=bar)
+        assert_close(f"dk[kv{kvh},g{g}]", to_f64(self.dk[0, :, kvh][idx]), dk)
+        assert_close(f"dv[kv{kvh},g{g}]", to_f64(self.dv[0, :, kvh][idx]), dv)
 
     def check_gradient_invariants(self, tol=2e-3):
         r = self.H // self.Hkv
@@ -122,14 +125,20 @@ def run_of(name):
     return _runs[name]
 
 
+def sample_units(heads, groups):
+    """Units (head, group) of a workload: the first and last head of each
+    half (H/2 - 1 and H/2 border the shift) in the first and last group."""
+    return [(h, g) for h in (0, heads // 2 - 1, heads // 2, heads - 1) for g in (0, groups - 1)]
+
+
 # ---------------------------------------------------------------- 7B, 32k
 
-@pytest.mark.parametrize("h,g", [(0, 0), (15, 3), (16, 0), (31, 3)])
+@pytest.mark.parametrize("h,g", sample_units(32, 4))
 def test_llama2_7b_32k_forward_units(h, g):
     run_of("llama2_7b_n32k").check_forward_unit(h, g)
 
 
-@pytest.mark.parametrize("kvh,g", [(0, 0), (16, 3), (31, 3)])
+@pytest.mark.parametrize("kvh,g", sample_units(32, 4))
 def test_llama2_7b_32k_backward_units(kvh, g):
     run_of("llama2_7b_n32k").check_backward_kv_group(kvh, g)
 
@@ -150,12 +159,14 @@ def test_llama2_7b_32k_deterministic():
 
 # --------------------------------------------------- 70B-style GQA + RoPE
 
-@pytest.mark.parametrize("h,g", [(0, 0), (31, 3), (32, 0), (63, 3)])
+@pytest.mark.parametrize("h,g", sample_units(64, 4))
 def test_gqa_rope_32k_forward_units(h, g):
     run_of("llama2_70b_gqa_n32k_rope").check_forward_unit(h, g)
 
 
-@pytest.mark.parametrize("kvh,g", [(0, 0), (7, 3)])
+# k/v heads 3 and 4 are the last unshifted and the first shifted one; each
+# is compared with all 8 of its q heads.
+@pytest.mark.parametrize("kvh,g", sample_units(8, 4))
 def test_gqa_rope_32k_backward_units(kvh, g):
     run_of("llama2_70b_gqa_n32k_rope").check_backward_kv_group(kvh, g)
 
@@ -166,12 +177,12 @@ def test_gqa_rope_32k_gradient_invariants():
 
 # ---------------------------------------------------------------- 7B, 100k
 
-@pytest.mark.parametrize("h,g", [(0, 0), (31, 3)])
+@pytest.mark.parametrize("h,g", sample_units(32, 4))
 def test_llama2_7b_100k_forward_units(h, g):
     run_of("llama2_7b_n100k").check_forward_unit(h, g)
 
 
-@pytest.mark.parametrize("kvh,g", [(0, 1), (31, 3)])
+@pytest.mark.parametrize("kvh,g", sample_units(32, 4))
 def test_llama2_7b_100k_backward_units(kvh, g):
     run_of("llama2_7b_n100k").check_backward_kv_group(kvh, g)
 

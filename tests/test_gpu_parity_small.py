@@ -12,7 +12,7 @@ import torch
 import oracle
 import workloads
 from grouped_shifted_attention_amd import ops
-from gpu_helpers import LSE_MAX_ABS, assert_close, kv_grad_max_abs, to_bits, to_f64, to_gpu
+from gpu_helpers import LSE_MAX_ABS, assert_close, to_bits, to_f64, to_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -73,8 +73,8 @@ def test_backward_matches_oracle(case):
     x64, got = _run(case)
     rq, rk, rv = oracle.s2attn_backward(x64["q"], x64["k"], x64["v"], x64["dout"], G, sh, rope=rope)
     assert_close("dq", to_f64(got["dq"]), rq)
-    assert_close("dk", to_f64(got["dk"]), rk, max_abs=kv_grad_max_abs(H, Hkv))
-    assert_close("dv", to_f64(got["dv"]), rv, max_abs=kv_grad_max_abs(H, Hkv))
+    assert_close("dk", to_f64(got["dk"]), rk)
+    assert_close("dv", to_f64(got["dv"]), rv)
 
 
 def test_tiny_workload_against_unrounded_fp32_inputs():
@@ -203,8 +203,8 @@ def test_autograd_wrapper_matches_oracle():
     rq, rk, rv = oracle.s2attn_backward(x64["q"], x64["k"], x64["v"], x64["dout"], G, G // 2)
     assert_close("out", to_f64(out.detach()), ref_o)
     assert_close("dq", to_f64(q.grad), rq)
-    assert_close("dk", to_f64(k.grad), rk, max_abs=kv_grad_max_abs(H, Hkv))
-    assert_close("dv", to_f64(v.grad), rv, max_abs=kv_grad_max_abs(H, Hkv))
+    assert_close("dk", to_f64(k.grad), rk)
+    assert_close("dv", to_f64(v.grad), rv)
 
 
 def test_backward_stages_equal_the_composite_call():
@@ -248,8 +248,8 @@ def test_alternate_heads_match_oracle(case):
     rq, rk, rv = oracle.s2attn_backward(x64["q"], x64["k"], x64["v"], x64["dout"], G, sh, rope=rope,
                                         head_pattern="alternate")
     assert_close("dq", to_f64(dq), rq)
-    assert_close("dk", to_f64(dk), rk, max_abs=kv_grad_max_abs(H, Hkv))
-    assert_close("dv", to_f64(dv), rv, max_abs=kv_grad_max_abs(H, Hkv))
+    assert_close("dk", to_f64(dk), rk)
+    assert_close("dv", to_f64(dv), rv)
 
 
 def test_general_entry_points_match_the_specific_ones():
