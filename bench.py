@@ -344,13 +344,13 @@ def main():
         ops.s2attn_fwd(q, k, v, G, sh, out=out, lse=lse)
         if events is not None:
             events[1].record(stream)
-        ops.s2attn_bwd_preprocess(q, out, do, lse, ws)
+        ops.s2attn_bwd_preprocess(out, do, lse, ws)
         if events is not None:
             events[2].record(stream)
-        ops.s2attn_bwd_dkdv(k, v, do, G, sh, ws, dk=dk, dv=dv)
+        ops.s2attn_bwd_dkdv(q, k, v, do, G, sh, ws, dk=dk, dv=dv)
         if events is not None:
             events[3].record(stream)
-        ops.s2attn_bwd_dq(k, v, do, G, sh, ws, dq=dq)
+        ops.s2attn_bwd_dq(q, k, v, do, G, sh, ws, dq=dq)
         if events is not None:
             events[4].record(stream)
 

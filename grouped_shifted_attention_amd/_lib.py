@@ -27,9 +27,9 @@ SIGNATURES = {
     "s2attn_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
     "s2attn_bwd_workspace_size": (_S, [_I, _I, _I, _I, _I]),
     "s2attn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _S, _P]),
-    "s2attn_bwd_preprocess": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _S, _P]),
-    "s2attn_bwd_dkdv": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _S, _P]),
-    "s2attn_bwd_dq": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _S, _P]),
+    "s2attn_bwd_preprocess": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _S, _P]),
+    "s2attn_bwd_dkdv": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _S, _P]),
+    "s2attn_bwd_dq": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _S, _P]),
     "s2attn_fwd_rope_workspace_size": (_S, [_I, _I, _I, _I, _I]),
     "s2attn_fwd_rope": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _D, _D, _P, _S, _P]),
     "s2attn_bwd_rope_workspace_size": (_S, [_I, _I, _I, _I, _I]),

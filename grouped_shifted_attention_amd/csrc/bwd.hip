@@ -116,12 +116,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const bool qvalid = qi < s.G;
   const int qpos = qvalid ? orig_pos(base, qi, s.N) : 0;
   const long long qoff = ((long long)(b * (long long)s.N + qpos) * s.H + h) * D;
-  // q arrives as q * c * log2(e) (the forward's rounding of it), so S comes
-  // out in log2 units.
+  // The q operand is q * c * log2(e) rounded to bf16 once (the forward's
+  // rounding of it), so S comes out in log2 units.  Without RoPE it is
+  // formed here from the caller's q; with RoPE the rotate pass formed it.
   bf16x8 qf[D / 16], dof[D / 16];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) {
     u32x4 qw = qvalid ? ld16(a.q + qoff + kk * 16 + hh * 8) : zero_u4();
+    if constexpr (!ROPE) qw = scale_bf16x8(qw, a.scale_log2);
     asm volatile("" : "+v"(qw));  // keep the fragment resident from here on
     qf[kk] = as_bf16x8(qw);
     dof[kk] = as_bf16x8(qvalid ? ld16(a.dout + qoff + kk * 16 + hh * 8) : zero_u4());
@@ -402,6 +404,8 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
       stg_stat[R] = (hh ? a.ndelta : a.nlse2)[so];
     }
   };
+  // Without RoPE the q chunks become the logit operand here: q * c * log2(e)
+  // with one bf16 rounding, as the forward forms it.
   auto swrite_step = [&](auto c, auto set) __attribute__((always_inline)) {
     constexpr int R = decltype(set)::value;
 #pragma unroll
@@ -409,7 +413,11 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
       const int item = tid + i * kThreads;
       const int tensor = item / kChunks;
       const int rem = item - tensor * kChunks;
-      st16((tensor ? obuf(c) : qbuf(c)) + (rem / kCh) * (D + 8) + (rem % kCh) * 8, stg[R][i]);
+      u32x4 w = stg[R][i];
+      if constexpr (!ROPE) {
+        if (tensor == 0) w = scale_bf16x8(w, a.scale_log2);
+      }
+      st16((tensor ? obuf(c) : qbuf(c)) + (rem / kCh) * (D + 8) + (rem % kCh) * 8, w);
     }
     if (wave == 0) stats(c)[lane] = stg_stat[R];
   };

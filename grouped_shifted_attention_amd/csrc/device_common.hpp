@@ -143,4 +143,13 @@ __device__ __forceinline__ u32x4 pack8(const float x[8]) {
   return __builtin_bit_cast(u32x4, cvt8(f));
 }
 
+// 8 bf16 values times a scale, rounded back to bf16 once.
+__device__ __forceinline__ u32x4 scale_bf16x8(u32x4 v, float scale) {
+  float x[8];
+  unpack8(v, x);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] *= scale;
+  return pack8(x);
+}
+
 }  // namespace s2a

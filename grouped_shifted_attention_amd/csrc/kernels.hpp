@@ -33,8 +33,10 @@ struct FwdArgs {
 };
 
 struct BwdArgs {
-  const uint16_t* q;     // [B, N, H, D]: q * c * log2(e) in bf16 (rotated first when rope is on), the
-                         // operand the forward's logits used (written by the preprocess pass)
+  const uint16_t* q;     // [B, N, H, D]: without RoPE the caller's q, which the kernels scale by
+                         // c * log2(e) with one bf16 rounding as they load it; with RoPE the
+                         // rotate pass's bf16(rotated q * c * log2(e)).  Either way the operand of
+                         // the forward's logits.
   const uint16_t* k;     // [B, N, Hkv, D] (rotated copy when rope is on)
   const uint16_t* v;
   const uint16_t* dout;  // [B, N, H, D]
@@ -51,10 +53,8 @@ struct BwdArgs {
 
 // Launchers: enqueue on `stream`, return the HIP status of the launch.
 hipError_t launch_fwd(const FwdArgs& a, const RopeTable* rope, hipStream_t stream);
-// Also writes qs = bf16(q * scale) when q is non-null (q and qs [B, N, H, D]).
 hipError_t launch_bwd_delta(const uint16_t* out, const uint16_t* dout, const float* lse, float* ndelta,
-                            float* nlse2, const uint16_t* q, uint16_t* qs, float scale, const Shape& s,
-                            hipStream_t stream);
+                            float* nlse2, const Shape& s, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, const RopeTable* rope, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, const RopeTable* rope, hipStream_t stream);
 // Rotate rows*heads*D bf16 values of a [B, N, heads, D] tensor into dst,

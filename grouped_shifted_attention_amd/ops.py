@@ -117,46 +117,46 @@ def s2attn_bwd(q, k, v, out, lse, dout, G, shift, dq=None, dk=None, dv=None, wor
     return dq, dk, dv
 
 
-def s2attn_bwd_preprocess(q, out, dout, lse, workspace):
-    """Stage 1 of the backward: the row statistics (-Delta, -lse*log2 e) and
-    the scaled copy of q into the workspace."""
+def s2attn_bwd_preprocess(out, dout, lse, workspace):
+    """Stage 1 of the backward: the row statistics (-Delta, -lse*log2 e) into
+    the workspace."""
     B, N, H, D = out.shape
-    _need(q, "q", torch.bfloat16, (B, N, H, D), None)
-    _need(out, "out", torch.bfloat16, (B, N, H, D), q.device)
-    _need(dout, "dout", torch.bfloat16, (B, N, H, D), q.device)
-    _need(lse, "lse", torch.float32, (B, H, N), q.device)
-    check(lib().s2attn_bwd_preprocess(_ptr(q), _ptr(out), _ptr(dout), _ptr(lse), B, N, H, D, _ptr(workspace),
+    _need(out, "out", torch.bfloat16, (B, N, H, D), None)
+    _need(dout, "dout", torch.bfloat16, (B, N, H, D), out.device)
+    _need(lse, "lse", torch.float32, (B, H, N), out.device)
+    check(lib().s2attn_bwd_preprocess(_ptr(out), _ptr(dout), _ptr(lse), B, N, H, D, _ptr(workspace),
                                       workspace.numel() * workspace.element_size(), _stream(out)))
 
 
-def _stage_dims(k, v, dout):
+def _stage_dims(q, k, v, dout):
     B, N, H, D = dout.shape
     _need(dout, "dout", torch.bfloat16, (B, N, H, D), None)
+    _need(q, "q", torch.bfloat16, (B, N, H, D), dout.device)
     Hkv = k.shape[2] if k.dim() == 4 else -1
     _need(k, "k", torch.bfloat16, (B, N, Hkv, D), dout.device)
     _need(v, "v", torch.bfloat16, (B, N, Hkv, D), dout.device)
     return B, N, H, Hkv, D
 
 
-def s2attn_bwd_dkdv(k, v, dout, G, shift, workspace, dk=None, dv=None):
+def s2attn_bwd_dkdv(q, k, v, dout, G, shift, workspace, dk=None, dv=None):
     """Stage 2 of the backward: dk, dv (needs the preprocess stage's workspace)."""
-    B, N, H, Hkv, D = _stage_dims(k, v, dout)
+    B, N, H, Hkv, D = _stage_dims(q, k, v, dout)
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     _need(dk, "dk", torch.bfloat16, (B, N, Hkv, D), k.device)
     _need(dv, "dv", torch.bfloat16, (B, N, Hkv, D), k.device)
-    check(lib().s2attn_bwd_dkdv(_ptr(k), _ptr(v), _ptr(dout), _ptr(dk), _ptr(dv),
+    check(lib().s2attn_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dk), _ptr(dv),
                                 B, N, H, Hkv, D, int(G), int(shift), _ptr(workspace),
                                 workspace.numel() * workspace.element_size(), _stream(k)))
     return dk, dv
 
 
-def s2attn_bwd_dq(k, v, dout, G, shift, workspace, dq=None):
+def s2attn_bwd_dq(q, k, v, dout, G, shift, workspace, dq=None):
     """Stage 3 of the backward: dq (needs the preprocess stage's workspace)."""
-    B, N, H, Hkv, D = _stage_dims(k, v, dout)
+    B, N, H, Hkv, D = _stage_dims(q, k, v, dout)
     dq = torch.empty_like(dout) if dq is None else dq
     _need(dq, "dq", torch.bfloat16, (B, N, H, D), k.device)
-    check(lib().s2attn_bwd_dq(_ptr(k), _ptr(v), _ptr(dout), _ptr(dq),
+    check(lib().s2attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq),
                               B, N, H, Hkv, D, int(G), int(shift), _ptr(workspace),
                               workspace.numel() * workspace.element_size(), _stream(k)))
     return dq

@@ -70,11 +70,8 @@ int s2attn_fwd(const void* q, const void* k, const void* v, void* out, float* ls
 
 /*
  * Workspace bytes s2attn_bwd needs: two float32 [B, H, N] row statistics,
- * -Delta[b, h, n] = -sum_d dout * out and -lse[b, h, n] * log2(e), then a
- * bf16 [B, N, H, D] copy of q * log2(e) / sqrt(D) (the q operand of the
- * forward's logits, rounded as the forward rounds it, so the backward
- * recomputes P from exactly the logits the forward normalised), each
- * starting on a 256-byte boundary.
+ * -Delta[b, h, n] = -sum_d dout * out and -lse[b, h, n] * log2(e), each
+ * starting on a 256-byte boundary (8 bytes per (b, h, n) row in all).
  */
 size_t s2attn_bwd_workspace_size(int B, int N, int H, int Hkv, int D);
 
@@ -84,7 +81,10 @@ size_t s2attn_bwd_workspace_size(int B, int N, int H, int Hkv, int D);
  * out and lse must be the forward's results for the same q, k, v.
  * dq, dk, dv are overwritten (not accumulated into).  `workspace` is device
  * memory of at least s2attn_bwd_workspace_size() bytes (256-byte aligned),
- * clobbered by the call.  Deterministic: no atomics.
+ * clobbered by the call.  The kernels recompute P from the forward's own
+ * logits (q times log2(e)/sqrt(D) rounded to bf16 once, formed as q is
+ * loaded), so each row of P sums to one against lse.  Deterministic: no
+ * atomics.
  */
 int s2attn_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
                const void* dout, void* dq, void* dk, void* dv,
@@ -95,23 +95,23 @@ int s2attn_bwd(const void* q, const void* k, const void* v, const void* out, con
  * The backward in stages: the same kernels s2attn_bwd enqueues, in the same
  * order, for callers that want to schedule or time them separately.
  *   s2attn_bwd_preprocess  the row statistics (-Delta, -lse*log2(e)) from
- *                          out, dout and the forward's lse, and the scaled
- *                          copy of q, into the workspace
- *   s2attn_bwd_dkdv        dk, dv (reads the workspace, not q)
- *   s2attn_bwd_dq          dq     (reads the workspace, not q)
+ *                          out, dout and the forward's lse, into the
+ *                          workspace
+ *   s2attn_bwd_dkdv        dk, dv
+ *   s2attn_bwd_dq          dq
  * dkdv and dq do not depend on each other and may run on different streams
- * once preprocess has completed.  Arguments and the workspace are those of
- * s2attn_bwd (workspace of s2attn_bwd_workspace_size() bytes); dkdv and dq
- * only read the workspace.
+ * once preprocess has completed; both only read the workspace.  Arguments
+ * and the workspace are those of s2attn_bwd (workspace of
+ * s2attn_bwd_workspace_size() bytes).
  */
-int s2attn_bwd_preprocess(const void* q, const void* out, const void* dout, const float* lse,
+int s2attn_bwd_preprocess(const void* out, const void* dout, const float* lse,
                           int B, int N, int H, int D,
                           void* workspace, size_t workspace_bytes, void* stream);
-int s2attn_bwd_dkdv(const void* k, const void* v, const void* dout,
+int s2attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
                     void* dk, void* dv,
                     int B, int N, int H, int Hkv, int D, int G, int shift,
                     const void* workspace, size_t workspace_bytes, void* stream);
-int s2attn_bwd_dq(const void* k, const void* v, const void* dout, void* dq,
+int s2attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout, void* dq,
                   int B, int N, int H, int Hkv, int D, int G, int shift,
                   const void* workspace, size_t workspace_bytes, void* stream);
 
@@ -136,8 +136,11 @@ int s2attn_fwd_rope(const void* q, const void* k, const void* v, void* out, floa
 /*
  * Backward of s2attn_fwd_rope: dq and dk are gradients w.r.t. the unrotated
  * q and k (passed back through the transposed rotation).  The workspace holds
- * the two row statistics, the rotated q times log2(e) / sqrt(D) and the
- * rotated k.
+ * the two row statistics, bf16(rotated q * log2(e)/sqrt(D)) and bf16(rotated
+ * k): q and k are rotated once per call by a pass of their own (every q row
+ * is re-read by each k/v tile of its group, every k row by each q tile, so
+ * rotating them inside those kernels would repeat the rotation G/128 and
+ * G/256 times over).
  */
 size_t s2attn_bwd_rope_workspace_size(int B, int N, int H, int Hkv, int D);
 int s2attn_bwd_rope(const void* q, const void* k, const void* v, const void* out,

@@ -124,8 +124,8 @@ def test_bwd_checks_workspace():
     L = _lib.lib()
     B, N, H, Hkv, D, G, sh = 1, 256, 4, 4, 64, 64, 32
     need = L.s2attn_bwd_workspace_size(B, N, H, Hkv, D)
-    # -Delta and -lse*log2(e) (fp32), then the scaled copy of q (bf16)
-    assert need >= 2 * B * H * N * 4 + B * N * H * D * 2 and need % 256 == 0
+    # -Delta and -lse*log2(e) (fp32), each 256-byte aligned; nothing else
+    assert need == 2 * ((B * H * N * 4 + 255) // 256 * 256)
     step = 1 << 24
     p = [0x10000000 + i * step for i in range(10)]
     st = L.s2attn_bwd(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7], p[8], B, N, H, Hkv, D, G, sh,
@@ -150,8 +150,8 @@ def test_workspace_sizes():
     br = L.s2attn_bwd_rope_workspace_size(B, N, H, Hkv, D)
     b = L.s2attn_bwd_workspace_size(B, N, H, Hkv, D)
     assert fr >= B * N * Hkv * D * 2
-    assert b >= 2 * B * H * N * 4 + B * N * H * D * 2
-    assert br >= b + B * N * Hkv * D * 2  # plus the rotated k
+    assert b == 2 * B * H * N * 4  # the two row statistics only
+    assert br >= b + B * N * H * D * 2 + B * N * Hkv * D * 2  # plus the rotated q and k
     assert L.s2attn_bwd_workspace_size(0, N, H, Hkv, D) == 0
 
 
@@ -261,3 +261,4 @@ def test_lora_bwd_rejects_bad_buffers():
     assert _lora_bwd(dx=FAKE + 11 * (1 << 28)) == EINVAL      # dx overlaps dq
     assert b"overlaps" in _lib.lib().s2attn_last_error()
     assert _lora_bwd(M=0) == _lib.S2ATTN_OK
+

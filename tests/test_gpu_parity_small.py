@@ -214,9 +214,9 @@ def test_backward_stages_equal_the_composite_call():
     out, lse = ops.s2attn_fwd(q, k, v, G, sh)
     dq, dk, dv = ops.s2attn_bwd(q, k, v, out, lse, do, G, sh)
     ws = ops.bwd_workspace(q, k)
-    ops.s2attn_bwd_preprocess(q, out, do, lse, ws)
-    dk2, dv2 = ops.s2attn_bwd_dkdv(k, v, do, G, sh, ws)
-    dq2 = ops.s2attn_bwd_dq(k, v, do, G, sh, ws)
+    ops.s2attn_bwd_preprocess(out, do, lse, ws)
+    dk2, dv2 = ops.s2attn_bwd_dkdv(q, k, v, do, G, sh, ws)
+    dq2 = ops.s2attn_bwd_dq(q, k, v, do, G, sh, ws)
     torch.cuda.synchronize()
     for a, b in ((dq, dq2), (dk, dk2), (dv, dv2)):
         assert np.array_equal(to_bits(a), to_bits(b))
