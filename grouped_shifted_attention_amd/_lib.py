@@ -27,6 +27,7 @@ SIGNATURES = {
     "s2attn_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
     "s2attn_bwd_workspace_size": (_S, [_I, _I, _I, _I, _I]),
     "s2attn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _S, _P]),
+    "s2attn_bwd_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
     "s2attn_bwd_preprocess": (_I, [_P, _P, _P, _I, _I, _I, _I, _P, _S, _P]),
     "s2attn_bwd_dkdv": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _S, _P]),
     "s2attn_bwd_dq": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _S, _P]),

@@ -8,6 +8,7 @@
 #include <cstdint>
 #include <cstring>
 #include <exception>
+#include <mutex>
 #include <string>
 
 #include "kernels.hpp"
@@ -276,6 +277,53 @@ size_t bwd_ws(int B, int N, int H, int Hkv, int D, bool rope) {
   return n;
 }
 
+// Device scratch of the entry point that allocates nothing
+// (s2attn_bwd_noalloc): the backward's two row statistics.  One copy per GPU
+// the library runs on, held until the process ends.  In host code `scratch`
+// is only a stand-in for the device symbol; its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+__device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Address of this device's scratch, looked up on the first call on it.
+int scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(S2ATTN_EUNSUPPORTED, "device index beyond the scratch table");
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (ptr == nullptr || ((uintptr_t)ptr & (kAlign - 1)) != 0)
+      return fail(S2ATTN_EHIP, "scratch address is null or not 256-byte aligned");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return S2ATTN_OK;
+}
+
+int do_bwd_noalloc(const void* q, const void* k, const void* v, const void* out, const float* lse, const void* dout,
+                   void* dq, void* dk, void* dv, int B, int N, int H, int Hkv, int D, int G, int shift,
+                   void* stream) {
+  int st = check_shape(B, N, H, Hkv, D, G, shift);
+  if (st) return st;
+  if (B == 0 || N == 0) return S2ATTN_OK;
+  const size_t need = bwd_ws(B, N, H, Hkv, D, false);
+  if (need > kScratchBytes)
+    return fail(S2ATTN_EINVAL, "s2attn_bwd_noalloc: the row statistics need " + std::to_string(need) +
+                                   " bytes, beyond its scratch of " + std::to_string(kScratchBytes) +
+                                   " (B*H*N must stay at or below " + std::to_string(kScratchBytes / 8) + ")");
+  void* ws = nullptr;
+  if ((st = scratch_for_current_device(&ws))) return st;
+  return do_bwd(q, k, v, out, lse, dout, dq, dk, dv, B, N, H, Hkv, D, G, shift, nullptr, ws, kScratchBytes, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -293,6 +341,14 @@ int s2attn_bwd(const void* q, const void* k, const void* v, const void* out, con
   return guarded([&] {
     return do_bwd(q, k, v, out, lse, dout, dq, dk, dv, B, N, H, Hkv, D, G, shift, nullptr, workspace,
                   workspace_bytes, stream);
+  });
+}
+
+int s2attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                       const void* dout, void* dq, void* dk, void* dv, int B, int N, int H, int Hkv, int D, int G,
+                       int shift, void* stream) {
+  return guarded([&] {
+    return do_bwd_noalloc(q, k, v, out, lse, dout, dq, dk, dv, B, N, H, Hkv, D, G, shift, stream);
   });
 }
 

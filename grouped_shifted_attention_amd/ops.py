@@ -117,6 +117,17 @@ def s2attn_bwd(q, k, v, out, lse, dout, G, shift, dq=None, dk=None, dv=None, wor
     return dq, dk, dv
 
 
+def s2attn_bwd_noalloc(q, k, v, out, lse, dout, G, shift, dq=None, dk=None, dv=None):
+    """s2attn_bwd without a workspace: the library's own device scratch holds
+    the row statistics (B*H*N <= 4,194,304; calls on one GPU must not
+    overlap).  Returns (dq, dk, dv)."""
+    (B, N, H, Hkv, D), dq, dk, dv = _bwd_common(q, k, v, out, lse, dout, dq, dk, dv)
+    check(lib().s2attn_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout),
+                                   _ptr(dq), _ptr(dk), _ptr(dv), B, N, H, Hkv, D, int(G), int(shift),
+                                   _stream(q)))
+    return dq, dk, dv
+
+
 def s2attn_bwd_preprocess(out, dout, lse, workspace):
     """Stage 1 of the backward: the row statistics (-Delta, -lse*log2 e) into
     the workspace."""

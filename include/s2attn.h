@@ -92,6 +92,22 @@ int s2attn_bwd(const void* q, const void* k, const void* v, const void* out, con
                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * s2attn_bwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation with no workspace argument.  The row statistics live in
+ * a device scratch array inside the library, 32 MiB per GPU, held from the
+ * first call on that GPU until the process ends; the call rejects
+ * (S2ATTN_EINVAL) shapes whose statistics exceed it, i.e. B*H*N above
+ * 4,194,304 rows.  It allocates nothing and calls no allocating routine.
+ * Every call on one GPU uses that GPU's one scratch array: calls that
+ * overlap on one GPU (other streams, other threads) race and must be
+ * serialised by the caller.  No RoPE; heads H/2 .. H-1 are shifted.
+ */
+int s2attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* out,
+                       const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                       int B, int N, int H, int Hkv, int D, int G, int shift, void* stream);
+
+/*
  * The backward in stages: the same kernels s2attn_bwd enqueues, in the same
  * order, for callers that want to schedule or time them separately.
  *   s2attn_bwd_preprocess  the row statistics (-Delta, -lse*log2(e)) from

@@ -262,3 +262,10 @@ def test_lora_bwd_rejects_bad_buffers():
     assert b"overlaps" in _lib.lib().s2attn_last_error()
     assert _lora_bwd(M=0) == _lib.S2ATTN_OK
 
+
+def test_noalloc_rejects_shapes_beyond_its_scratch():
+    # 5 * 4 * 2^20 rows of statistics need 160 MiB: rejected before any HIP call.
+    L = _lib.lib()
+    st = L.s2attn_bwd_noalloc(*([FAKE] * 9), 5, 1 << 20, 4, 4, 64, 1024, 512, None)
+    assert st == EINVAL and "scratch" in detail()
+    assert L.s2attn_bwd_noalloc(*([FAKE] * 9), 0, 256, 4, 4, 64, 64, 32, None) == 0  # empty call
