@@ -5,6 +5,7 @@ fallback path.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -58,21 +59,39 @@ class S2AttnError(RuntimeError):
         super().__init__(f"s2attn status {status}: {detail}")
 
 
+def load(path: str) -> ctypes.CDLL:
+    """Open a build of the library at `path` with the ABI's signatures."""
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is not built; run `python -m grouped_shifted_attention_amd.build` "
+            "(or __graft_entry__.build()) first")
+    handle = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(handle, name)
+        fn.restype = res
+        fn.argtypes = args
+    return handle
+
+
 def lib() -> ctypes.CDLL:
     """Load libs2attn.so once; raise if it is missing."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(
-                f"{LIB_PATH} is not built; run `python -m grouped_shifted_attention_amd.build` "
-                "(or __graft_entry__.build()) first")
-        handle = ctypes.CDLL(LIB_PATH)
-        for name, (res, args) in SIGNATURES.items():
-            fn = getattr(handle, name)
-            fn.restype = res
-            fn.argtypes = args
-        _lib = handle
+        _lib = load(LIB_PATH)
     return _lib
+
+
+@contextlib.contextmanager
+def using(handle: ctypes.CDLL):
+    """Route the binding's calls to another build of the library (the
+    race-check build) for the duration of a with-block."""
+    global _lib
+    saved = lib()
+    _lib = handle
+    try:
+        yield handle
+    finally:
+        _lib = saved
 
 
 def check(status: int) -> None:

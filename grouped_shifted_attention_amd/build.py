@@ -19,6 +19,10 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libs2attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
+# Race-check build: the same sources with S2A_DEBUG_BARRIERS, which turns every
+# LDS hand-over into a full drain-and-barrier; its results must equal the
+# normal build's bit for bit (tests/test_gpu_race_check.py).
+DEBUG_LIB_PATH = os.path.join(PKG, "libs2attn_debugbarriers.so")
 
 SOURCES = ["api.cpp", "fwd.hip", "bwd.hip", "bwd_delta.hip", "rope.hip", "lora_qkv.hip", "lora_bwd.hip"]
 HEADERS = ["device_common.hpp", "kernels.hpp", "staging.hpp", "lora_kernels.hpp"]
@@ -79,5 +83,12 @@ def build(verbose: bool = False, defines=(), out_path: str = LIB_PATH, build_dir
     return out_path
 
 
+def build_all(verbose: bool = False) -> list:
+    """The product library and the race-check build next to it."""
+    return [build(verbose),
+            build(verbose, defines=("S2A_DEBUG_BARRIERS",), out_path=DEBUG_LIB_PATH,
+                  build_dir=os.path.join(ROOT, "_build", "debugbarriers"))]
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv[1:]))
+    print(build_all(verbose="-v" in sys.argv[1:]))

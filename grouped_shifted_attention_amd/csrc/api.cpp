@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 #include <exception>
 #include <mutex>
@@ -25,6 +26,17 @@ int fail(int status, const std::string& msg) {
 
 int hip_fail(hipError_t e, const char* what) {
   return fail(S2ATTN_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// Test hook for the HIP-error status path: when S2ATTN_TEST_HIP_ERROR names
+// a nonzero hipError_t code, every call that has passed its argument checks
+// fails with S2ATTN_EHIP before making any HIP call, as a failed launch would.
+int injected_hip_error() {
+  const char* v = std::getenv("S2ATTN_TEST_HIP_ERROR");
+  if (v == nullptr || *v == '\0') return S2ATTN_OK;
+  const long code = std::strtol(v, nullptr, 10);
+  if (code == 0) return S2ATTN_OK;
+  return fail(S2ATTN_EHIP, "HIP error " + std::to_string(code) + " (injected by S2ATTN_TEST_HIP_ERROR)");
 }
 
 template <class F>
@@ -133,6 +145,7 @@ int do_fwd(const void* q, const void* k, const void* v, void* out, float* lse, i
   if (st) return st;
   if (rope && ws_bytes < round_up(kb)) return fail(S2ATTN_EINVAL, "workspace too small");
   if (rope && ((uintptr_t)ws & (kAlign - 1)) != 0) return fail(S2ATTN_EINVAL, "workspace is not 256-byte aligned");
+  if ((st = injected_hip_error())) return st;
   const hipStream_t s = (hipStream_t)stream;
   s2a::FwdArgs a{};
   a.q = (const uint16_t*)q;
@@ -172,6 +185,7 @@ int do_bwd(const void* q, const void* k, const void* v, const void* out, const f
   if (st) return st;
   if (ws_bytes < need) return fail(S2ATTN_EINVAL, "workspace too small");
   if (((uintptr_t)ws & (kAlign - 1)) != 0) return fail(S2ATTN_EINVAL, "workspace is not 256-byte aligned");
+  if ((st = injected_hip_error())) return st;
   const hipStream_t s = (hipStream_t)stream;
   char* w = (char*)ws;
   float* ndelta = (float*)w;
@@ -248,16 +262,19 @@ int do_bwd_stage(Stage stage, const void* q, const void* k, const void* v, const
     Buf in[3] = {{out, qb, "out"}, {dout, qb, "dout"}, {lse, sb, "lse"}};
     Buf outs[1] = {{ws, need, "workspace"}};
     if ((st = check_buffers(in, 3, outs, 1))) return st;
+    if ((st = injected_hip_error())) return st;
     e = s2a::launch_bwd_delta((const uint16_t*)out, a.dout, lse, ndelta, nlse2, a.s, s);
   } else if (stage == Stage::kDkdv) {
     Buf in[5] = {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"}, {dout, qb, "dout"}, {ws, need, "workspace"}};
     Buf outs[2] = {{dk, kb, "dk"}, {dv, kb, "dv"}};
     if ((st = check_buffers(in, 5, outs, 2))) return st;
+    if ((st = injected_hip_error())) return st;
     e = s2a::launch_bwd_dkdv(a, nullptr, s);
   } else {
     Buf in[5] = {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"}, {dout, qb, "dout"}, {ws, need, "workspace"}};
     Buf outs[1] = {{dq, qb, "dq"}};
     if ((st = check_buffers(in, 5, outs, 1))) return st;
+    if ((st = injected_hip_error())) return st;
     e = s2a::launch_bwd_dq(a, nullptr, s);
   }
   if (e != hipSuccess) return hip_fail(e, "backward stage");
@@ -319,6 +336,7 @@ int do_bwd_noalloc(const void* q, const void* k, const void* v, const void* out,
     return fail(S2ATTN_EINVAL, "s2attn_bwd_noalloc: the row statistics need " + std::to_string(need) +
                                    " bytes, beyond its scratch of " + std::to_string(kScratchBytes) +
                                    " (B*H*N must stay at or below " + std::to_string(kScratchBytes / 8) + ")");
+  if ((st = injected_hip_error())) return st;
   void* ws = nullptr;
   if ((st = scratch_for_current_device(&ws))) return st;
   return do_bwd(q, k, v, out, lse, dout, dq, dk, dv, B, N, H, Hkv, D, G, shift, nullptr, ws, kScratchBytes, stream);
@@ -483,6 +501,7 @@ int s2attn_lora_qkv_fwd(const void* x, int M, int d_in, const void* wq_t, const 
     a.r = r;
     a.scale = (float)scale;
     a.t = r > 0 ? (uint16_t*)workspace : nullptr;
+    if (int ist = injected_hip_error()) return ist;
     hipError_t e = s2a::launch_lora_qkv(a, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "lora_qkv launch");
     return (int)S2ATTN_OK;
@@ -569,6 +588,7 @@ int s2attn_lora_qkv_bwd(const void* x, int M, int d_in, const void* wq_t, const 
       a.dts = (uint16_t*)workspace;
       a.part = (float*)((char*)workspace + round_up(tb));
     }
+    if (int ist = injected_hip_error()) return ist;
     hipError_t e = s2a::launch_lora_qkv_bwd(a, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "lora_qkv_bwd launch");
     return (int)S2ATTN_OK;

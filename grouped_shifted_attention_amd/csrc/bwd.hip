@@ -603,7 +603,11 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
       }
     }
     if (n + 2 < nsteps) swrite_step(std::integral_constant<int, (C + 2) % 6>{}, std::integral_constant<int, C & 1>{});
+#ifdef S2A_DEBUG_BARRIERS
+    lds_barrier();  // race-check build: a full barrier after every step
+#else
     if constexpr ((C & 1) != 0) lds_barrier();
+#endif
   };
   auto run = [&](auto role) __attribute__((always_inline)) {
     for (int n = 0; n <= nsteps + 1; n += 6) {

@@ -130,7 +130,18 @@ __device__ __forceinline__ void wait_vmem_all() { wait_vmcnt<0>(); }
 // to-LDS loads included), so loads of later tiles stay in flight across it;
 // callers first wait (vmcnt) for the tile the next step reads.  The "memory"
 // clobber keeps the compiler from moving memory accesses across it.
+#ifdef S2A_DEBUG_BARRIERS
+// Race-check build: every LDS hand-over drains all outstanding memory
+// operations (global loads and direct-to-LDS loads included) and meets a full
+// workgroup barrier.  Its results must equal the normal build's bit for bit;
+// a difference exposes a hand-over that relies on a missing wait or barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+}
+#else
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+#endif
 
 // wait_vmcnt for a wave-uniform count known only at run time (0..16; larger
 // counts wait for everything, which is always safe).

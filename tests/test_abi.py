@@ -269,3 +269,27 @@ def test_noalloc_rejects_shapes_beyond_its_scratch():
     st = L.s2attn_bwd_noalloc(*([FAKE] * 9), 5, 1 << 20, 4, 4, 64, 1024, 512, None)
     assert st == EINVAL and "scratch" in detail()
     assert L.s2attn_bwd_noalloc(*([FAKE] * 9), 0, 256, 4, 4, 64, 64, 32, None) == 0  # empty call
+
+
+def test_hip_error_status_path(monkeypatch):
+    # A HIP failure after the argument checks maps to S2ATTN_EHIP with its
+    # detail; the hook fails the call before any HIP call, so this runs
+    # without a GPU.
+    L = _lib.lib()
+    monkeypatch.setenv("S2ATTN_TEST_HIP_ERROR", "719")
+    B, N, H, Hkv, D, G, sh = 1, 256, 4, 4, 64, 64, 32
+    st = L.s2attn_fwd(FAKE, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000, None, B, N, H, Hkv, D, G, sh, None)
+    assert st == _lib.S2ATTN_EHIP and "HIP error 719" in detail()
+    p = [0x10000000 + i * (1 << 24) for i in range(10)]
+    need = L.s2attn_bwd_workspace_size(B, N, H, Hkv, D)
+    st = L.s2attn_bwd(*p[:9], B, N, H, Hkv, D, G, sh, p[9], need, None)
+    assert st == _lib.S2ATTN_EHIP and "injected" in detail()
+    st = L.s2attn_bwd_noalloc(*p[:9], B, N, H, Hkv, D, G, sh, None)
+    assert st == _lib.S2ATTN_EHIP
+    with pytest.raises(_lib.S2AttnError, match="HIP error 719"):
+        _lib.check(st)
+    # invalid arguments are still reported as such, ahead of the hook
+    st = L.s2attn_fwd(FAKE, FAKE, FAKE, FAKE, None, B, N, H, Hkv, D, 100, sh, None)
+    assert st == EINVAL
+    monkeypatch.setenv("S2ATTN_TEST_HIP_ERROR", "0")
+    assert L.s2attn_fwd(FAKE, FAKE, FAKE, FAKE, None, 0, N, H, Hkv, D, G, sh, None) == 0
