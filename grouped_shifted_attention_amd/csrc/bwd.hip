@@ -378,12 +378,16 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
   u32x4 stg[2][kPer];
   float stg_stat[2] = {0.f, 0.f};
   // Steps are loaded in order; (ld_hi, ld_i0) is the q head and first row of
-  // the next one (a running count, no division per step).
+  // the next one (a running count, no division per step).  Every interval
+  // issues the same loads, also past the last step (those read the last q
+  // head's rows and land in stages nobody reads): with no branch around
+  // them the compiler's wait before each LDS write counts only the older
+  // register set, instead of waiting for the loads just issued as well.
   int ld_hi = 0, ld_i0 = key_start;
   const int row_stop = key_start + steps_per_head * kBMQ;
   auto gload_step = [&](auto set) __attribute__((always_inline)) {
     constexpr int R = decltype(set)::value;
-    const int hi = ld_hi, i0 = ld_i0;
+    const int hi = min(ld_hi, rq - 1), i0 = ld_i0;
     ld_i0 += kBMQ;
     if (ld_i0 == row_stop) {
       ld_i0 = key_start;
@@ -398,7 +402,7 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
       const int row = min(i0 + rem / kCh, s.G - 1);
       stg[R][i] = ld16((tensor ? a.dout : a.q) + head_off + orig_pos(base, row, s.N) * q_row + (rem % kCh) * 8);
     }
-    if (wave == 0) {
+    {  // every wave loads (equal load counts per wave); wave 0 writes
       const int i = min(i0 + rowperm32(l32), s.G - 1);
       const long long so = ((long long)b * s.H + h0 + hi) * s.N + orig_pos(base, i, s.N);
       stg_stat[R] = (hh ? a.ndelta : a.nlse2)[so];
@@ -527,7 +531,7 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
     const f16x8 ph1 = __builtin_bit_cast(f16x8, Pbuf[step & 3][pair][1][lane]);
     float ds[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) ds[r] = (float)(r < 8 ? ph0[r] : ph1[r - 8]) * dp[r];
+    for (int r = 0; r < 16; ++r) ds[r] = __builtin_fmaf((float)(r < 8 ? ph0[r] : ph1[r - 8]), dp[r], 0.f);  // v_fma_mix
     const f32x8 dsf[2] = {f32x8{ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]},
                           f32x8{ds[8], ds[9], ds[10], ds[11], ds[12], ds[13], ds[14], ds[15]}};
     bf16x8 dsb[2];
@@ -566,15 +570,11 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
   using R1 = std::integral_constant<int, 1>;
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
-  if (nsteps > 0) {
-    gload_step(R0{});
-    swrite_step(S0{}, R0{});
-  }
-  if (nsteps > 1) {
-    gload_step(R1{});
-    swrite_step(S1{}, R1{});
-  }
-  if (nsteps > 2) gload_step(R0{});
+  gload_step(R0{});
+  swrite_step(S0{}, R0{});
+  gload_step(R1{});
+  swrite_step(S1{}, R1{});
+  gload_step(R0{});
   lds_barrier();
 
   // Step n (stage c = n % 6): the P wave does step n, the dS wave step n-2;
@@ -592,7 +592,7 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
   auto iter = [&](int n, auto c, auto role) __attribute__((always_inline)) {
     constexpr int C = decltype(c)::value;
     constexpr bool DS = decltype(role)::value;
-    if (n + 3 < nsteps) gload_step(std::integral_constant<int, (C + 1) & 1>{});
+    gload_step(std::integral_constant<int, (C + 1) & 1>{});
     if constexpr (!DS) {
       if (n < nsteps) p_step(n, key_start + cur_j * kBMQ, step_kind(cur_j) != 2, c);
       cur_j = cur_j + 1 == steps_per_head ? 0 : cur_j + 1;
@@ -602,7 +602,7 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
         ds_j = ds_j + 1 == steps_per_head ? 0 : ds_j + 1;
       }
     }
-    if (n + 2 < nsteps) swrite_step(std::integral_constant<int, (C + 2) % 6>{}, std::integral_constant<int, C & 1>{});
+    swrite_step(std::integral_constant<int, (C + 2) % 6>{}, std::integral_constant<int, C & 1>{});
 #ifdef S2A_DEBUG_BARRIERS
     lds_barrier();  // race-check build: a full barrier after every step
 #else
