@@ -660,7 +660,7 @@ hipError_t launch_dkdv_t(BwdArgs a, const RopeTable* rope, hipStream_t stream) {
 }  // namespace
 
 #ifndef S2A_DQ_WAVES_LARGE
-#define S2A_DQ_WAVES_LARGE 4  // waves per workgroup for groups longer than 1024
+#define S2A_DQ_WAVES_LARGE 8  // waves per workgroup for groups longer than 1024
 #endif
 
 template <int D, bool ROPE>
