@@ -379,15 +379,16 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
   float stg_stat[2] = {0.f, 0.f};
   // Steps are loaded in order; (ld_hi, ld_i0) is the q head and first row of
   // the next one (a running count, no division per step).  Every interval
-  // issues the same loads, also past the last step (those read the last q
-  // head's rows and land in stages nobody reads): with no branch around
-  // them the compiler's wait before each LDS write counts only the older
-  // register set, instead of waiting for the loads just issued as well.
+  // issues the same loads, also past the last step (those re-read the last
+  // step's rows, still in L2, into stages nobody reads): with no branch
+  // around them the compiler's wait before each LDS write counts only the
+  // older register set, instead of waiting for the loads just issued as well.
   int ld_hi = 0, ld_i0 = key_start;
   const int row_stop = key_start + steps_per_head * kBMQ;
   auto gload_step = [&](auto set) __attribute__((always_inline)) {
     constexpr int R = decltype(set)::value;
-    const int hi = min(ld_hi, rq - 1), i0 = ld_i0;
+    const bool past = ld_hi >= rq;
+    const int hi = past ? rq - 1 : ld_hi, i0 = past ? row_stop - kBMQ : ld_i0;
     ld_i0 += kBMQ;
     if (ld_i0 == row_stop) {
       ld_i0 = key_start;
