@@ -390,6 +390,8 @@ def main():
         if (rec.get("kernel") == dominant and rec.get("workload") == name
                 and rec.get("source_sha256") == kernel_source_digest()):
             roofline["traffic"] = rec["traffic_bytes"]
+            roofline["traffic_source"] = ("not measured in this run: FETCH_SIZE + WRITE_SIZE counter passes of a "
+                                          "separate profiled run on the same kernel sources, " + rec.get("source", ""))
     except (OSError, ValueError, KeyError):
         pass
 
