@@ -354,8 +354,15 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) acc[i] = zero16();
 
-  // Steps: every q head sharing this k/v head x every 32-row block from the
-  // first row that can see this tile's keys to the group end.
+  // Steps: every 32-row block from the first row that can see this tile's
+  // keys to the group end x every q head sharing this k/v head.  The row
+  // blocks go from the group end down (heads inner), so the workgroups of a
+  // unit, which run side by side on one XCD and all start at the group end,
+  // read the same q/dout tiles at the same time and share them in L2; each
+  // stops at its own diagonal.  (Walking up from each diagonal, head by
+  // head, put them on different heads within a few steps: under 8:1
+  // grouped-query sharing a unit's q/dout rows do not fit in L2, and the
+  // kernel read 25x its algorithmic bytes from HBM.)
   const int steps_per_head = (s.G - key_start + kBMQ - 1) / kBMQ;
   const int nsteps = steps_per_head * rq;
 
@@ -377,22 +384,20 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
   constexpr int kPer = 2 * kChunks / kThreads;
   u32x4 stg[2][kPer];
   float stg_stat[2] = {0.f, 0.f};
-  // Steps are loaded in order; (ld_hi, ld_i0) is the q head and first row of
-  // the next one (a running count, no division per step).  Every interval
+  // Steps are loaded in order; (ld_j, ld_hi) is the row block and q head of
+  // the next one (running counts, no division per step).  Every interval
   // issues the same loads, also past the last step (those re-read the last
   // step's rows, still in L2, into stages nobody reads): with no branch
   // around them the compiler's wait before each LDS write counts only the
   // older register set, instead of waiting for the loads just issued as well.
-  int ld_hi = 0, ld_i0 = key_start;
-  const int row_stop = key_start + steps_per_head * kBMQ;
+  int ld_j = steps_per_head - 1, ld_hi = 0;
   auto gload_step = [&](auto set) __attribute__((always_inline)) {
     constexpr int R = decltype(set)::value;
-    const bool past = ld_hi >= rq;
-    const int hi = past ? rq - 1 : ld_hi, i0 = past ? row_stop - kBMQ : ld_i0;
-    ld_i0 += kBMQ;
-    if (ld_i0 == row_stop) {
-      ld_i0 = key_start;
-      ++ld_hi;
+    const bool past = ld_j < 0;
+    const int hi = past ? rq - 1 : ld_hi, i0 = key_start + (past ? 0 : ld_j) * kBMQ;
+    if (++ld_hi == rq) {
+      ld_hi = 0;
+      --ld_j;
     }
     const long long head_off = (long long)b * s.N * q_row + (long long)(h0 + hi) * D;
 #pragma unroll
@@ -560,12 +565,12 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
   const int skip = min(steps_per_head, (kw0 - key_start) / kBMQ);
   const int diag_end = min(steps_per_head, (kw0 + 31 - key_start) / kBMQ + 1);
   const int ragged = ((s.G - key_start) % kBMQ) != 0 ? steps_per_head - 1 : steps_per_head;
-  // j: a step's index inside its q head's block sequence.
+  // j: a step's row block, counted from key_start.
   auto step_kind = [&](int j) __attribute__((always_inline)) {  // 0 skip, 1 masked, 2 full
     return j < skip ? 0 : ((j < diag_end || j >= ragged) ? 1 : 2);
   };
-  int cur_j = 0;  // j of step n (P wave)
-  int ds_j = 0;   // j of step n - 2 (dS wave)
+  int cur_j = steps_per_head - 1, cur_hi = 0;  // row block and q head of step n (P wave)
+  int ds_j = steps_per_head - 1, ds_hi = 0;    // of step n - 2 (dS wave)
 
   using R0 = std::integral_constant<int, 0>;
   using R1 = std::integral_constant<int, 1>;
@@ -596,11 +601,17 @@ __global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu
     gload_step(std::integral_constant<int, (C + 1) & 1>{});
     if constexpr (!DS) {
       if (n < nsteps) p_step(n, key_start + cur_j * kBMQ, step_kind(cur_j) != 2, c);
-      cur_j = cur_j + 1 == steps_per_head ? 0 : cur_j + 1;
+      if (++cur_hi == rq) {
+        cur_hi = 0;
+        --cur_j;
+      }
     } else {
       if (n >= 2) {
         ds_step(n - 2, step_kind(ds_j) != 2, std::integral_constant<int, (C + 4) % 6>{});
-        ds_j = ds_j + 1 == steps_per_head ? 0 : ds_j + 1;
+        if (++ds_hi == rq) {
+          ds_hi = 0;
+          --ds_j;
+        }
       }
     }
     swrite_step(std::integral_constant<int, (C + 2) % 6>{}, std::integral_constant<int, C & 1>{});
