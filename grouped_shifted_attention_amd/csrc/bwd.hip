@@ -100,10 +100,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int logical = xcd_logical_id(blockIdx.x, gridDim.x);
   const int unit = logical / a.tiles;
   const int t = a.tiles - 1 - (logical - unit * a.tiles);
-  const int g = unit % s.NG;
-  const int bh = unit / s.NG;
-  const int h = bh % s.H;
-  const int b = bh / s.H;
+  const QUnit uq = decode_q_unit(unit, s);
+  const int g = uq.g, h = uq.h, b = uq.b;
   const int sh = head_shift(h, s);
   const int kvh = h / (s.H / s.Hkv);
   const int base = g * s.G + sh;

@@ -104,6 +104,21 @@ __device__ __forceinline__ int head_shift(int h, const Shape& s) {
   return shifted ? s.shift : 0;
 }
 
+// Unit (b, q head h, group g) of a forward or dQ workgroup, from the unit
+// index.  The q heads that share a k/v head are adjacent (order b, k/v head,
+// g, q head within the k/v head), so consecutive units -- one XCD's
+// contiguous range of work items -- read the same k/v rows and share them in
+// L2.  Without grouped-query sharing this is the order (b, h, g).
+struct QUnit {
+  int b, h, g;
+};
+__device__ __forceinline__ QUnit decode_q_unit(int unit, const Shape& s) {
+  const int rq = s.H / s.Hkv;
+  const int hi = unit % rq, rest = unit / rq;
+  const int g = rest % s.NG, bk = rest / s.NG;
+  return QUnit{bk / s.Hkv, (bk % s.Hkv) * rq + hi, g};
+}
+
 // Original sequence position of local row j of a group whose first rolled
 // row sits at `base` = g*G + shift_h (< N).  The roll by -shift is circular
 // and base + j < 2N, so one conditional subtraction folds it.
