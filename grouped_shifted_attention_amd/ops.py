@@ -122,9 +122,11 @@ def s2attn_bwd_noalloc(q, k, v, out, lse, dout, G, shift, dq=None, dk=None, dv=N
     the row statistics (B*H*N <= 4,194,304; calls on one GPU must not
     overlap).  Returns (dq, dk, dv)."""
     (B, N, H, Hkv, D), dq, dk, dv = _bwd_common(q, k, v, out, lse, dout, dq, dk, dv)
-    check(lib().s2attn_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout),
-                                   _ptr(dq), _ptr(dk), _ptr(dv), B, N, H, Hkv, D, int(G), int(shift),
-                                   _stream(q)))
+    # The library takes the scratch of the current device: make it q's.
+    with torch.cuda.device(q.device):
+        check(lib().s2attn_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout),
+                                       _ptr(dq), _ptr(dk), _ptr(dv), B, N, H, Hkv, D, int(G), int(shift),
+                                       _stream(q)))
     return dq, dk, dv
 
 

@@ -101,7 +101,9 @@ int s2attn_bwd(const void* q, const void* k, const void* v, const void* out, con
  * 4,194,304 rows.  It allocates nothing and calls no allocating routine.
  * Every call on one GPU uses that GPU's one scratch array: calls that
  * overlap on one GPU (other streams, other threads) race and must be
- * serialised by the caller.  No RoPE; heads H/2 .. H-1 are shifted.
+ * serialised by the caller.  The scratch used is that of the calling
+ * thread's current HIP device, so stream (and every tensor) must belong to
+ * that device.  No RoPE; heads H/2 .. H-1 are shifted.
  */
 int s2attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* out,
                        const float* lse, const void* dout, void* dq, void* dk, void* dv,
