@@ -252,7 +252,7 @@ def bench_lora(args, name):
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": name, "M": M, "d_in": d_in, "widths": list(widths), "r": r, "scale": s,
-                   "parallelism": "single-gpu"},
+                   "parallelism": "single-gpu", "operands": args.operands},
         "pct_peak": 100.0 * value / PEAK_BF16_TFLOPS,
         "fwd_tflops": ffl / (fwd_ms * 1e-3) / 1e12,
         "bwd_tflops": bfl / (bwd_ms * 1e-3) / 1e12,
@@ -279,6 +279,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0)
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    ap.add_argument("--operands", default="normal",
+                    help="input operand variant (workloads.OPERAND_VARIANTS): normal (the benchmark), "
+                         "mant2 or paired_keys, for measuring data-dependent matrix-core throughput")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -306,7 +309,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    x = workloads.make_inputs(B, N, H, Hkv, D, seed=0)
+    x = workloads.make_inputs(B, N, H, Hkv, D, seed=0, operands=args.operands)
     to_gpu = lambda bits: torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
     q, k, v, do = (to_gpu(x[n]) for n in ("q", "k", "v", "dout"))
     out = torch.empty_like(q)
@@ -410,7 +413,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": name, "B": B, "N": N, "H": H, "Hkv": Hkv, "D": D, "G": G, "shift": sh,
                    "rope": list(rope) if rope is not None else None, "head_pattern": pattern,
-                   "parallelism": "single-gpu"},
+                   "parallelism": "single-gpu", "operands": args.operands},
         "pct_peak": 100.0 * value / PEAK_BF16_TFLOPS,
         "fwd_tflops": f_fwd / (kernel_ms[kernels[0]] * 1e-3) / 1e12,
         "bwd_tflops": f_bwd / (sum(kernel_ms[kk] for kk in kernels[1:]) * 1e-3) / 1e12,

@@ -216,11 +216,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
   };
 
-  // Step n: load tile n+1 into the other buffer, compute tile n, wait for
-  // tile n+1, barrier.  Unrolled by two so each step names its buffer.
+  // K/V tile walk: up from key 0 or down from the diagonal, alternating
+  // between consecutive units so that a unit's workgroups, which either start
+  // together or end together, stay on the same k/v tile in L2 (as in the
+  // forward kernel).
+  const bool walk_down = (unit & 1) != 0;
+  auto tile_at = [&](int i) __attribute__((always_inline)) { return walk_down ? ntiles - 1 - i : i; };
+
+  // Step i: load the tile of step i+1 into the other buffer, compute the tile
+  // of step i, wait for the load, barrier.  Unrolled by two so each step
+  // names its buffer.
   auto step = [&](int n, auto mask_tag, auto p) __attribute__((always_inline)) {
-    if (n + 1 < ntiles) load_tile(n + 1, std::integral_constant<bool, !decltype(p)::value>{});
-    compute(n, mask_tag, p);
+    if (n + 1 < ntiles) load_tile(tile_at(n + 1), std::integral_constant<bool, !decltype(p)::value>{});
+    compute(tile_at(n), mask_tag, p);
     wait_vmem_all();
     lds_barrier();
   };
@@ -233,14 +241,20 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     if (n < n1) step(n, mask_tag, P0{});
   };
 
-  load_tile(0, P0{});
+  load_tile(tile_at(0), P0{});
   wait_vmem_all();
   lds_barrier();
 
-  // Unmasked tiles first, then the diagonal ones (see the forward kernel).
+  // Tiles before n_full lie wholly left of this wave's diagonal and need no
+  // mask; walking up they come first, walking down last.
   const int n_full = min(ntiles, (wave_q0 + 1) / kBN);
-  run(0, n_full, std::false_type{});
-  run(n_full, ntiles, std::true_type{});
+  if (walk_down) {
+    run(0, ntiles - n_full, std::true_type{});
+    run(ntiles - n_full, ntiles, std::false_type{});
+  } else {
+    run(0, n_full, std::false_type{});
+    run(n_full, ntiles, std::true_type{});
+  }
 
   if (qvalid) store_row_acc<D, ROPE>(a.dq + qoff, dq, a.scale, hh, qpos, rope);
 }

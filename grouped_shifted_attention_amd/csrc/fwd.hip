@@ -414,6 +414,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int T = (rows_end + kBN - 1) / kBN;
   // Tiles before n_full lie wholly left of this wave's diagonal.
   const int n_full = min(T, (wave_q0 + 1) / kBN);
+  // Key-tile walk direction.  A unit's workgroups either start together (the
+  // first unit on an XCD, and each unit after one whose workgroups all ended
+  // together) or one after another as the previous unit's shorter workgroups
+  // end, the longest first.  Walking up from key 0 keeps the first kind on the
+  // same k/v tile at the same time, walking down from the diagonal does so for
+  // the second (each then ends together), so alternating the direction between
+  // consecutive units lets the unit's workgroups share each k/v tile in L2
+  // instead of re-reading the head's k/v rows from HBM at staggered times.
+  const bool walk_down = (unit & 1) != 0;
+  auto tile_at = [&](int i) __attribute__((always_inline)) { return walk_down ? T - 1 - i : i; };
 
   // ---- matrix phase ----
   // S^T(m) = K(m) Q^T: K fragments read (KD - 1) k-steps ahead of their
@@ -577,7 +587,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // Matrix phase m has no PV part for m = 0 and only the PV part for m = T.
   auto step = [&](int m, auto c) __attribute__((always_inline)) {
     using Cn = std::integral_constant<bool, !decltype(c)::value>;
-    if (m + 1 < T) gload(m + 1);
+    // Issued in every step (the last re-reads the final tile, still in L2),
+    // so no branch sits around the loads and the wait before the staging
+    // write counts only them.
+    gload(tile_at(min(m + 1, T - 1)));
     if (m >= 1) mat_pv(vbuf(Cn{}));
     if (m < T) mat_s(kbuf(c));
     if (m < T) slot_barrier();
@@ -589,11 +602,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (m + 1 < T) swrite(grp ? vbuf(Cn{}) : kbuf(Cn{}));
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) vpre[db] = vfrag(vbuf(c), db);  // V(m): visible since its write slot ended
-      softmax(m);
+      softmax(tile_at(m));
       if (grp == 0 || m + 1 < T) slot_barrier();
     }
   };
-  gload(0);
+  gload(tile_at(0));
   swrite(grp ? Vs0 : Ks0);
   slot_barrier();
   if (grp) slot_barrier();

@@ -69,12 +69,26 @@ def f64_from_bf16_bits(bits: np.ndarray) -> np.ndarray:
     return u.view(np.float32).astype(np.float64)
 
 
-def make_inputs(B, N, H, Hkv, D, seed=0, with_dout=True, qk_prescale=None):
+# Operand variants of the same draws, for measuring how the matrix cores'
+# throughput depends on the bits they multiply (the method is unchanged):
+#   "normal"       the N(0,1) draws rounded to bfloat16 (every workload's data);
+#   "mant2"        each bfloat16 value of q, k, v, dout keeps only the top 2 of
+#                  its 7 stored mantissa bits (truncated toward zero);
+#   "paired_keys"  in k and v, the rows at positions 64n+32 .. 64n+63 repeat the
+#                  rows at 64n .. 64n+31, so the two 32-key halves of every
+#                  64-key tile hold the same values.
+OPERAND_VARIANTS = ("normal", "mant2", "paired_keys")
+
+
+def make_inputs(B, N, H, Hkv, D, seed=0, with_dout=True, qk_prescale=None, operands="normal"):
     """Seeded bfloat16 inputs as uint16 bit arrays.
 
     ``qk_prescale`` (optional float) multiplies the float32 q and k draws
-    before rounding; it changes only the data, never the method.
+    before rounding; ``operands`` picks one of ``OPERAND_VARIANTS``.  Both
+    change only the data, never the method.
     """
+    if operands not in OPERAND_VARIANTS:
+        raise ValueError(f"operands must be one of {OPERAND_VARIANTS}, not {operands!r}")
     rng = np.random.default_rng(seed)
     out = {}
     for name, heads in (("q", H), ("k", Hkv), ("v", Hkv)):
@@ -84,6 +98,13 @@ def make_inputs(B, N, H, Hkv, D, seed=0, with_dout=True, qk_prescale=None):
         out[name] = bf16_bits_from_f32(x)
     if with_dout:
         out["dout"] = bf16_bits_from_f32(rng.standard_normal((B, N, H, D), dtype=np.float32))
+    if operands == "mant2":
+        for name in out:
+            out[name] = out[name] & np.uint16(0xFFE0)
+    elif operands == "paired_keys":
+        for name in ("k", "v"):
+            rows = np.arange((N // 64) * 64).reshape(-1, 64)[:, 32:].ravel()
+            out[name][:, rows] = out[name][:, rows - 32]
     return out
 
 
