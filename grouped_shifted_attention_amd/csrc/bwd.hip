@@ -217,10 +217,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   };
 
   // K/V tile walk: up from key 0 or down from the diagonal, alternating
-  // between consecutive units so that a unit's workgroups, which either start
-  // together or end together, stay on the same k/v tile in L2 (as in the
-  // forward kernel).
-  const bool walk_down = (unit & 1) != 0;
+  // between consecutive units when a unit's workgroups fit on one XCD's CUs,
+  // so that they, which then either start together or end together, stay on
+  // the same k/v tile in L2 (as in the forward kernel).
+  const bool walk_down = a.tiles <= kCusPerXcd && (unit & 1) != 0;
   auto tile_at = [&](int i) __attribute__((always_inline)) { return walk_down ? ntiles - 1 - i : i; };
 
   // Step i: load the tile of step i+1 into the other buffer, compute the tile

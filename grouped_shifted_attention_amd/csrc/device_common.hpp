@@ -30,6 +30,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, WGs dispatched round-robin
+constexpr int kCusPerXcd = 32;  // MI355X: 256 compute units over the 8 dies
 
 __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);

@@ -414,15 +414,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int T = (rows_end + kBN - 1) / kBN;
   // Tiles before n_full lie wholly left of this wave's diagonal.
   const int n_full = min(T, (wave_q0 + 1) / kBN);
-  // Key-tile walk direction.  A unit's workgroups either start together (the
-  // first unit on an XCD, and each unit after one whose workgroups all ended
-  // together) or one after another as the previous unit's shorter workgroups
-  // end, the longest first.  Walking up from key 0 keeps the first kind on the
-  // same k/v tile at the same time, walking down from the diagonal does so for
-  // the second (each then ends together), so alternating the direction between
-  // consecutive units lets the unit's workgroups share each k/v tile in L2
-  // instead of re-reading the head's k/v rows from HBM at staggered times.
-  const bool walk_down = (unit & 1) != 0;
+  // Key-tile walk direction.  When a unit's workgroups fit on one XCD's CUs,
+  // they either start together (the first unit on an XCD, and each unit after
+  // one whose workgroups all ended together) or one after another as the
+  // previous unit's shorter workgroups end, the longest first.  Walking up
+  // from key 0 keeps the first kind on the same k/v tile at the same time,
+  // walking down from the diagonal does so for the second (each then ends
+  // together), so alternating the direction between consecutive units lets a
+  // unit's workgroups share each k/v tile in L2 instead of re-reading the
+  // head's k/v rows from HBM at staggered times.  Units of more workgroups
+  // than an XCD has CUs keep walking up, which re-reads less for them.
+  const bool walk_down = a.tiles <= kCusPerXcd && (unit & 1) != 0;
   auto tile_at = [&](int i) __attribute__((always_inline)) { return walk_down ? T - 1 - i : i; };
 
   // ---- matrix phase ----
