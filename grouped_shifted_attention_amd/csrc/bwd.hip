@@ -177,6 +177,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // row-major K tile.
 #pragma unroll
     for (int kb = 0; kb < kBN / 32; ++kb) {
+      // A masked half whose keys all follow this wave's last row adds exact
+      // zeros to dQ: skip it (the workgroup's later waves need those keys).
+      if constexpr (MASK) {
+        if (key0 + kb * 32 > wave_q0 + 31) continue;
+      }
       f32x16 sc, dp;
       {
         bf16x8 kf[2], vf[2];
