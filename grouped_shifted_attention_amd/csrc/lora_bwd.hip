@@ -113,6 +113,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int kWRowStep = 512 / Sh::WChunks;
   const int ncol = min(n0 + wc * 8, a.N - 8);  // clamped column (never stored past N)
   u32x4 xr[4], wr[Sh::WPer];
+  int mrow[4];  // the thread's token rows (clamped)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) mrow[i] = min(m0 + trow + 64 * i, a.M - 1);
   auto gload = [&](int kt) {
     // Segment of tile kt (wave-uniform; selected field by field so the
     // parameter block stays in scalar registers).
@@ -122,9 +125,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (s == 2 && t >= ntiles[2]) { t -= ntiles[2]; s = 3; }
     const LoraBwdSeg g = s == 0 ? a.seg[0] : (s == 1 ? a.seg[1] : (s == 2 ? a.seg[2] : a.seg[3]));
     const int k0 = t * kBK;
+    if (k0 + kBK <= g.len && g.stack >= g.len) {
+      // A whole tile of one weight: no bounds checks, one pointer.
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xr[i] = ld16(g.tok + (long long)mrow[i] * g.ldt + k0 + tc * 8);
+      const uint16_t* wb = g.w[0] + (long long)k0 * g.ldw + ncol;
+#pragma unroll
+      for (int i = 0; i < Sh::WPer; ++i) wr[i] = ld16(wb + (wrow + kWRowStep * i) * g.ldw);
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int m = min(m0 + trow + 64 * i, a.M - 1);
+      const int m = mrow[i];
       const int k = k0 + tc * 8;
       const bool ok = k < g.len;
       const u32x4 v = ld16(g.tok + (long long)m * g.ldt + (ok ? k : 0));
@@ -135,7 +147,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const int k = k0 + wrow + kWRowStep * i;
       const bool ok = k < g.len;
       const int kk = ok ? k : 0;
-      const int p = kk / g.stack;  // stacked weights: g.stack rows per pointer
+      // Stacked weights: g.stack rows per pointer, so kk < 3 * g.stack (and
+      // g.stack = len for a single weight); two compares, no division.
+      const int p = (kk >= g.stack) + (kk >= 2 * g.stack);
       const uint16_t* wp = p == 0 ? g.w[0] : (p == 1 ? g.w[1] : g.w[2]);
       const u32x4 v = ld16(wp + (long long)(kk - p * g.stack) * g.ldw + ncol);
       wr[i] = ok ? v : zero_u4();
