@@ -40,9 +40,8 @@ __device__ __forceinline__ void rope_unrotate4(float x[4], int pos, const double
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
     const double r = (double)pos * rev[(d0 >> 1) + e];
-    const float ang = (float)((r - floor(r)) * 6.283185307179586);
     float sn, cs;
-    sincosf(ang, &sn, &cs);
+    sincos_turns((float)(r - floor(r)), sn, cs);
     const float a = x[2 * e], b = x[2 * e + 1];
     x[2 * e] = a * cs + b * sn;
     x[2 * e + 1] = -a * sn + b * cs;

@@ -128,17 +128,24 @@ __device__ __forceinline__ int orig_pos(int base, int j, int N) {
   return p >= N ? p - N : p;
 }
 
+// Sine and cosine of an angle given in turns, t in [0, 1]: the hardware's
+// v_sin_f32 / v_cos_f32 take their argument in turns.
+__device__ __forceinline__ void sincos_turns(float t, float& sn, float& cs) {
+  sn = __builtin_amdgcn_sinf(t);
+  cs = __builtin_amdgcn_cosf(t);
+}
+
 // RoPE: rotate the 4 pairs held in 8 consecutive bf16 (d0 .. d0+7, d0 even)
 // of a row at original position `pos`.  rev[i] = base^(-2i/D) / (s * 2*pi)
 // is the pair's frequency in revolutions per position; the angle is reduced
-// in float64 before the float32 sine and cosine.
+// to a fraction of a turn in float64 before the float32 sine and cosine.
 __device__ __forceinline__ void rope_rotate8(float x[8], int pos, const double* rev, int d0, bool inverse) {
+  const double p = (double)pos;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const double r = (double)pos * rev[(d0 >> 1) + e];
-    const float ang = (float)((r - floor(r)) * 6.283185307179586);
+    const double r = p * rev[(d0 >> 1) + e];
     float sn, cs;
-    sincosf(ang, &sn, &cs);
+    sincos_turns((float)(r - floor(r)), sn, cs);
     if (inverse) sn = -sn;
     const float a = x[2 * e], b = x[2 * e + 1];
     x[2 * e] = a * cs - b * sn;
