@@ -688,12 +688,12 @@ hipError_t launch_dkdv_t(BwdArgs a, const RopeTable* rope, hipStream_t stream) {
 }  // namespace
 
 #ifndef S2A_DQ_WAVES_LARGE
-#define S2A_DQ_WAVES_LARGE 8  // waves per workgroup for groups longer than 1024
+#define S2A_DQ_WAVES_LARGE 8  // waves per workgroup for groups longer than 2048
 #endif
 
 template <int D, bool ROPE>
 hipError_t launch_dq_d(const BwdArgs& a, const RopeTable* rope, hipStream_t stream) {
-  if (a.s.G <= 1024) return launch_dq_t<D, 4, ROPE>(a, rope, stream);
+  if (a.s.G <= 2048) return launch_dq_t<D, 4, ROPE>(a, rope, stream);
   return launch_dq_t<D, S2A_DQ_WAVES_LARGE, ROPE>(a, rope, stream);
 }
 

@@ -18,7 +18,7 @@
 // Computing S^T (not S) leaves each lane with one query row, so the softmax
 // statistics and the rescale of O are per-lane scalars.
 //
-// Groups of up to 1024 rows: fwd_kernel, 2 or 4 waves, tiles loaded straight
+// Groups of up to 2048 rows: fwd_kernel, 2 or 4 waves, tiles loaded straight
 // into LDS.  Longer groups: fwd_pp_kernel, 8 waves in two groups whose
 // matrix and softmax phases alternate on each SIMD.
 #include "device_common.hpp"
@@ -662,7 +662,10 @@ hipError_t launch_fwd_t(FwdArgs a, const RopeTable* rope, hipStream_t stream) {
 template <int D, bool ROPE>
 hipError_t launch_fwd_d(const FwdArgs& a, const RopeTable* rope, hipStream_t stream) {
   if (a.s.G <= 64) return launch_fwd_t<D, 2, 1, ROPE>(a, rope, stream);
-  if (a.s.G <= 1024) return launch_fwd_t<D, 4, 1, ROPE>(a, rope, stream);
+  // Up to 2048 rows the 4-wave kernel, with twice the workgroups, finishes
+  // first (about 9% at G = 2048); from 4096 rows on the two run level or the
+  // 8-wave kernel leads.
+  if (a.s.G <= 2048) return launch_fwd_t<D, 4, 1, ROPE>(a, rope, stream);
   return launch_fwd_pp<D, ROPE>(a, rope, stream);
 }
 
