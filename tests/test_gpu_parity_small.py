@@ -39,6 +39,10 @@ CASES = [
     ("rope_pi25_to_100k", 1, 102400, 2, 2, 128, 4096, 2048, (10000.0, 25.0)),
     ("rope_base8_gqa", 1, 2048, 4, 2, 128, 512, 256, (80000.0, 1.0)),
     ("dense_g4096_large_tiles", 1, 4096, 2, 2, 128, 4096, 0, None),
+    # Groups longer than 2048 rows take the eight-wave forward and dQ: a
+    # ragged D = 64 group, and grouped-query sharing with RoPE.
+    ("ragged_g2200_eight_wave_d64", 1, 4400, 2, 2, 64, 2200, 1100, None),
+    ("gqa_rope_g3072_eight_wave", 1, 6144, 4, 2, 128, 3072, 1536, (10000.0, 8.0)),
 ]
 IDS = [c[0] for c in CASES]
 
@@ -223,12 +227,14 @@ def test_backward_stages_equal_the_composite_call():
 
 
 # Alternate-head shifting through the general entry points: without sharing
-# (odd H included, and the eight-wave kernel), with grouped-query sharing and
-# RoPE, and with one k/v head (no head is then shifted).
+# (odd H included, with the four- and the eight-wave kernels), with
+# grouped-query sharing and RoPE, and with one k/v head (no head is then
+# shifted).
 ALT_CASES = [
     ("alt_mha", 1, 512, 4, 4, 64, 128, 64, None),
     ("alt_gqa_rope", 1, 1024, 8, 4, 128, 256, 128, (10000.0, 8.0)),
     ("alt_odd_heads_large_tiles", 1, 4096, 3, 3, 128, 2048, 1024, None),
+    ("alt_odd_heads_eight_wave", 1, 5120, 3, 3, 128, 2560, 1280, None),
     ("alt_mqa", 1, 512, 4, 1, 64, 128, 64, None),
 ]
 
