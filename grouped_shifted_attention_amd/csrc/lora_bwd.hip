@@ -85,8 +85,16 @@ __device__ __forceinline__ void tile_coords(int id, int mt, int nt, int& tm, int
   tm = band * kBand + (rem - tn * rows);
 }
 
+// Up to three products of the same output shape in one launch, the product
+// picked by blockIdx.y: the three s dy_p B_p^T products each have only
+// ceil(M / 256) output tiles (r columns), too few to fill the chip alone.
+struct LoraBwdK1Batch {
+  LoraBwdK1Args arg[3];
+};
+
 template <int BN>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void lora_bwd_k1(LoraBwdK1Args a) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void lora_bwd_k1(LoraBwdK1Batch batch) {
+  const LoraBwdK1Args& a = batch.arg[blockIdx.y];
   using Sh = K1Shape<BN>;
   constexpr int kBN = BN;
   constexpr int kWStride = Sh::WStride;
@@ -328,11 +336,13 @@ __global__ __launch_bounds__(256) void lora_bwd_k3(const float* __restrict__ par
   out[i * si + j * sj] = (uint16_t)(w[0] & 0xffffu);
 }
 
+// `count` products of the same M and N (batch.arg[0 .. count-1]).
 template <int BN>
-hipError_t launch_k1(const LoraBwdK1Args& a, hipStream_t stream) {
+hipError_t launch_k1(const LoraBwdK1Batch& batch, int count, hipStream_t stream) {
+  const LoraBwdK1Args& a = batch.arg[0];
   const long long grid = (long long)((a.M + kBM - 1) / kBM) * ((a.N + BN - 1) / BN);
-  if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(lora_bwd_k1<BN>, dim3((unsigned)grid), dim3(512), 0, stream, a);
+  if (grid <= 0 || count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(lora_bwd_k1<BN>, dim3((unsigned)grid, (unsigned)count), dim3(512), 0, stream, batch);
   return hipGetLastError();
 }
 
@@ -361,8 +371,10 @@ hipError_t launch_lora_qkv_bwd(const LoraQkvBwdArgs& q, hipStream_t stream) {
   hipError_t e;
   if (q.r > 0) {
     // dT_s = s dy_p B_p^T into the workspace, target p in columns p r ..
+    // (the three products in one launch).
+    LoraBwdK1Batch kb{};
     for (int p = 0; p < 3; ++p) {
-      LoraBwdK1Args k{};
+      LoraBwdK1Args& k = kb.arg[p];
       k.M = q.M;
       k.N = q.r;
       k.out = q.dts + p * q.r;
@@ -370,11 +382,12 @@ hipError_t launch_lora_qkv_bwd(const LoraQkvBwdArgs& q, hipStream_t stream) {
       k.scale = q.scale;
       k.nseg = 1;
       k.seg[0] = LoraBwdSeg{q.dy[p], q.width[p], {q.bt[p], q.bt[p], q.bt[p]}, q.r, q.width[p], q.width[p]};
-      if ((e = launch_k1<64>(k, stream)) != hipSuccess) return e;
     }
+    if ((e = launch_k1<64>(kb, 3, stream)) != hipSuccess) return e;
   }
   // dx = sum_p dy_p W_p^T (+ dT_s A^T).
-  LoraBwdK1Args k{};
+  LoraBwdK1Batch xb{};
+  LoraBwdK1Args& k = xb.arg[0];
   k.M = q.M;
   k.N = q.K;
   k.out = q.dx;
@@ -384,7 +397,7 @@ hipError_t launch_lora_qkv_bwd(const LoraQkvBwdArgs& q, hipStream_t stream) {
   for (int p = 0; p < 3; ++p)
     k.seg[k.nseg++] = LoraBwdSeg{q.dy[p], q.width[p], {q.wt[p], q.wt[p], q.wt[p]}, q.K, q.width[p], q.width[p]};
   if (q.r > 0) k.seg[k.nseg++] = LoraBwdSeg{q.dts, 3 * q.r, {q.at[0], q.at[1], q.at[2]}, q.K, 3 * q.r, q.r};
-  if ((e = launch_k1<256>(k, stream)) != hipSuccess) return e;
+  if ((e = launch_k1<256>(xb, 1, stream)) != hipSuccess) return e;
   if (q.r == 0) return hipSuccess;
   const int splits = lora_bwd_splits(q.M);
   const int rps = ((q.M + splits - 1) / splits + kK2K - 1) / kK2K * kK2K;
