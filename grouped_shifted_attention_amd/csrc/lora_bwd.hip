@@ -4,7 +4,7 @@
 // y_p = x W_p + T_p B_p.  With the frozen W, the gradients for the upstream
 // gradients dy_p are (the calculus of that forward; the pages do not spell
 // out a backward):
-//   dT_s = s dy_p B_p^T                  [M, 3r]   (K1, one launch per target)
+//   dT_s = s dy_p B_p^T                  [M, 3r]   (K1, the three targets in one launch)
 //   dx   = sum_p dy_p W_p^T + dT_s A^T   [M, d_in] (K1, one launch)
 //   dB_p = T_p^T dy_p                    stored as B_p^T: [width_p, r] (K2 + K3)
 //   dA_p = x^T dT_s,p                    stored as A_p^T: [r, d_in]   (K2 + K3)
